@@ -60,12 +60,12 @@ def write_rows(cache_bits, x_bits, slots, block_size):
     """cache[slot // bs, :, slot % bs, :] = x[t] for each token t with slot >= 0.
 
     cache_bits: [N, H, bs, D]; x_bits: [T, H, D] of the same bit type.
+    Slots of one call are distinct.
     """
-    for t, s in enumerate(slots):
-        s = int(s)
-        if s < 0:
-            continue
-        cache_bits[s // block_size, :, s % block_size, :] = x_bits[t]
+    slots = np.asarray(slots, dtype=np.int64)
+    t = np.nonzero(slots >= 0)[0]
+    s = slots[t]
+    cache_bits[s // block_size, :, s % block_size, :] = np.asarray(x_bits)[t]
     return cache_bits
 
 
@@ -73,15 +73,14 @@ def write_rows_fp8(cache_codes, x_f32, slots, scales, block_size):
     """fp8 store: code = RNE-saturate(x / scale[block, head]), x in float32.
 
     cache_codes: [N, H, bs, D] uint8; x_f32: [T, H, D] float32 values;
-    scales: [N, H] float32, the block's existing scale.
+    scales: [N, H] float32, the block's existing scale.  Slots are distinct.
     """
-    for t, s in enumerate(slots):
-        s = int(s)
-        if s < 0:
-            continue
-        blk = s // block_size
-        for h in range(x_f32.shape[1]):
-            cache_codes[blk, h, s % block_size, :] = fp8.quantize_f32(x_f32[t, h], scales[blk, h])
+    slots = np.asarray(slots, dtype=np.int64)
+    t = np.nonzero(slots >= 0)[0]
+    s = slots[t]
+    blk, off = s // block_size, s % block_size
+    codes = fp8.quantize_f32(np.asarray(x_f32, dtype=np.float32)[t], scales[blk][:, :, None])
+    cache_codes[blk, :, off, :] = codes
     return cache_codes
 
 
