@@ -1,0 +1,244 @@
+/*
+ * pa.h -- C ABI of libpa.so, paged attention for AMD Instinct MI355X (gfx950).
+ *
+ * The KV cache is split into fixed-size blocks of tokens that sit anywhere in
+ * one physical pool; each sequence's block table maps its logical blocks to
+ * physical ones and its length truncates the last, partly filled block
+ * (vLLM course ch. 4 "PagedAttention core idea"; DataWhale llm-algo-leetcode
+ * (5) notes, "vLLM PagedAttention" section 3).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Device pointers are owned by the caller (e.g. torch tensors).  The GPU
+ *   calls never allocate, free or synchronise device memory; every launch goes
+ *   on the caller's stream and returns before the GPU work ends.
+ * - Every call returns pa_status.  0 is success, negative is an error; nothing
+ *   is launched when an argument check fails.  pa_last_error() returns a
+ *   message for the last failing call of the calling thread.  Faults inside a
+ *   kernel surface at the caller's next synchronisation of the stream.
+ * - Host-side checks: null pointers, dtype combinations, head_dim in {64,128},
+ *   block_size in {4,8,16,32}, 16-byte alignment of every device pointer,
+ *   workspace size.  Block-table entries and slots are trusted: the caller
+ *   keeps them in [0, num_blocks) (the allocator below produces only such).
+ * - Pool layout: K and V are each [num_blocks][num_heads][block_size][head_dim]
+ *   of kv_dtype, so one (block, head) tile is contiguous (block_size*head_dim
+ *   elements; 4 KiB for 16 x 128 fp16).  Pool bases must be 128-byte aligned,
+ *   the alignment the course ch. 4 pitfall note asks for.
+ * - fp8 pools (PA_FP8_E4M3, OCP E4M3FN, max 448) carry one float32 scale per
+ *   (block, head) for K and one for V: value = code * scale (the blog
+ *   article's mixed-precision KV storage, section 2.3).
+ * - The host allocator is an opaque handle; it is not thread safe; on error
+ *   it changes no state.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* bad argument; nothing launched, no state changed */
+  PA_ERR_OOM = -2,         /* the free list cannot satisfy the request */
+  PA_ERR_UNSUPPORTED = -3, /* valid but not built (dtype / shape combination) */
+  PA_ERR_HIP = -4,         /* the HIP runtime reported an error on launch */
+  PA_ERR_NO_SEQ = -5       /* unknown sequence id */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3 /* OCP E4M3FN */
+} pa_dtype;
+
+/* One layer's paged pool.  All pointers are device pointers. */
+typedef struct pa_pool {
+  void* k_cache;      /* [num_blocks][num_heads][block_size][head_dim] kv_dtype */
+  void* v_cache;      /* same shape as k_cache */
+  float* k_scale;     /* [num_blocks][num_heads], fp8 pools only, else NULL */
+  float* v_scale;     /* [num_blocks][num_heads], fp8 pools only, else NULL */
+  int32_t num_blocks;
+  int32_t num_heads;
+  int32_t block_size; /* tokens per block: 4, 8, 16 or 32 */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t kv_dtype;   /* pa_dtype */
+} pa_pool;
+
+/* ---------------------------------------------------------------- GPU calls */
+
+/*
+ * pa_reshape_and_cache -- write new K/V rows into their pool slots.
+ * Slot s is block s / block_size, row s % block_size (vLLM course ch. 4,
+ * attention pseudocode: the block table gives the physical block, the row
+ * inside it is the token's offset).
+ *   key, value    device, [num_tokens][num_heads][head_dim] of in_dtype,
+ *                 contiguous.  For f32/f16/bf16 pools in_dtype must equal
+ *                 kv_dtype and the rows are copied bit for bit.  For fp8 pools
+ *                 in_dtype is f32, f16 or bf16 and each element is stored as
+ *                 RNE-saturate(x / scale[block][head]) with the division in
+ *                 float32; the block's scale must already be set.
+ *   slot_mapping  device, [num_tokens] int64; a negative slot skips the row.
+ * Two rows of one call must not name the same slot.
+ */
+pa_status pa_reshape_and_cache(const pa_pool* pool, const void* key, const void* value,
+                               int32_t in_dtype, const int64_t* slot_mapping,
+                               int32_t num_tokens, hipStream_t stream);
+
+/*
+ * pa_copy_blocks -- whole-block copy of K and V (and of the fp8 scales) for
+ * each (src, dst) pair, the copy that copy-on-write needs before a sequence
+ * writes into a block it shares (DataWhale notes section 4, copy-on-write).
+ *   src_dst   device, [num_pairs][2] int32.  Pairs are independent: no dst may
+ *             be another pair's src or dst.
+ */
+pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t num_pairs,
+                         hipStream_t stream);
+
+/*
+ * Partition size chosen by pa_decode when partition_blocks == 0, for this
+ * pool and batch.  Exposed so that callers can size the workspace.
+ */
+int32_t pa_decode_auto_partition_blocks(const pa_pool* pool, int32_t num_seqs,
+                                        int32_t max_blocks_per_seq);
+
+/*
+ * Bytes of device workspace pa_decode needs for these arguments (0 when every
+ * sequence fits in one partition).  The workspace holds per-partition partial
+ * results and one counter per (sequence, head).
+ */
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, int32_t partition_blocks);
+
+/*
+ * pa_decode_workspace_init -- zero the counters of a fresh workspace (a small
+ * kernel on the stream; no memset node).  Every complete pa_decode call leaves
+ * them zero again, so this is needed once after allocating the workspace.
+ */
+pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_decode -- attention of one query token per sequence over its paged K/V
+ * (blog article section 3.2.2 forward pass at one query row; vLLM course
+ * ch. 4 attention pseudocode).  For sequence i and head h, with L = context
+ * length (every cached token, the current one included):
+ *     out[i][h] = sum_j softmax_j(scale * <q[i][h], K_i[j][h]>) V_i[j][h],
+ * j over 0..L-1 gathered through the block table; L = 0 gives zeros.
+ *   out           device, [num_seqs][num_heads][head_dim] of out_dtype
+ *                 (f32, or q_dtype).
+ *   q             device, [num_seqs][num_heads][head_dim] of q_dtype
+ *                 (kv_dtype for f32/f16/bf16 pools; f32/f16/bf16 for fp8).
+ *   block_tables  device, [num_seqs][max_blocks_per_seq] int32; only the first
+ *                 ceil(L / block_size) entries of a row are read.
+ *   context_lens  device, [num_seqs] int32, 0 <= L <= max_blocks_per_seq*block_size.
+ *   partition_blocks  blocks per split-K partition (0 = automatic).  Sequences
+ *                 longer than one partition are split; the partials are merged
+ *                 with a running-max / running-sum reduction inside the same
+ *                 kernel (the last partition of a (sequence, head) to finish
+ *                 does the merge).
+ *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, counters
+ *                 zeroed once by pa_decode_workspace_init.  Calls that share a
+ *                 workspace must be ordered (same stream).
+ */
+pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                    const pa_pool* pool, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    float scale, int32_t partition_blocks, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_prefill_chunk -- causal attention of a chunk of query tokens against the
+ * sequence's paged context (blog article section 3.2.2 forward pass with its
+ * causal mask; the mask is aligned so that the chunk's rows are the last
+ * S_i positions of a sequence of L_i tokens: row r sees keys 0 .. L_i - S_i + r).
+ * The chunk's own K/V must already be in the pool.
+ *   q, out            device, packed [total_q][num_heads][head_dim]; sequence
+ *                     i owns rows query_start_loc[i] .. query_start_loc[i+1]-1.
+ *                     q_dtype = kv_dtype in {f16, bf16}; out_dtype f32 or q_dtype.
+ *   query_start_loc   device, [num_seqs + 1] int32, non-decreasing, from 0.
+ *   context_lens      device, [num_seqs] int32, L_i >= S_i (chunk included).
+ *   max_query_len     host bound on every S_i (sizes the grid).
+ */
+pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                           const pa_pool* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs,
+                           int32_t max_query_len, float scale, hipStream_t stream);
+
+/* ------------------------------------------------------ host block allocator */
+
+/*
+ * The block manager of the pages: a free list of physical blocks, one block
+ * table per sequence, ceil(n / block_size) blocks for a prompt, one more block
+ * when a decode step crosses a block boundary, "OOM" when the free list runs
+ * short, blocks returned when a sequence ends (DataWhale notes, KVCacheManager
+ * exercise; vLLM course ch. 4 "Block management strategy" table and allocation
+ * flow), and copy-on-write sharing of prefix blocks (DataWhale notes section 4).
+ * The free list is FIFO: blocks are taken from its front, freed blocks go to
+ * its back in table order.  All pointers here are host pointers.
+ */
+typedef struct pa_allocator pa_allocator;
+
+/* initial_free_order: [num_blocks] permutation of 0..num_blocks-1, or NULL for
+ * 0, 1, ..., num_blocks-1. */
+pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
+                              const int32_t* initial_free_order, pa_allocator** out);
+void pa_allocator_destroy(pa_allocator* a);
+
+/* New sequence of num_tokens tokens (ceil(num_tokens / block_size) blocks,
+ * all or nothing).  slots_out: [num_tokens] or NULL. */
+pa_status pa_alloc_prompt(pa_allocator* a, int64_t seq_id, int32_t num_tokens,
+                          int64_t* slots_out);
+
+/* Append n tokens.  If the last block is partly filled and shared, one fresh
+ * block is taken first and (src, dst) is returned for a whole-block copy
+ * (cow_src_dst[2], *num_cow = 1; else *num_cow = 0); then
+ * ceil((L+n)/bs) - ceil(L/bs) new blocks.  slots_out: [n] or NULL. */
+pa_status pa_append_tokens(pa_allocator* a, int64_t seq_id, int32_t n, int64_t* slots_out,
+                           int32_t* cow_src_dst, int32_t* num_cow);
+
+/* Append n tokens to each of num_seqs distinct sequences, all or nothing
+ * (the whole batch is checked against the free list first).  slots_out:
+ * [num_seqs][n]; cow_pairs_out: [num_seqs][2] (a sequence's pair, or -1 -1);
+ * *num_cow: number of copies. */
+pa_status pa_append_tokens_batch(pa_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                                 int32_t n, int64_t* slots_out, int32_t* cow_pairs_out,
+                                 int32_t* num_cow);
+
+/* The child shares every block of the parent (reference count + 1). */
+pa_status pa_fork(pa_allocator* a, int64_t parent_id, int64_t child_id);
+
+/* Drop the sequence; blocks whose reference count reaches 0 return to the back
+ * of the free list in table order. */
+pa_status pa_free_seq(pa_allocator* a, int64_t seq_id);
+
+/* Copy a block table out: up to cap entries into out, *len = table length,
+ * *seq_len = tokens (either output may be NULL). */
+pa_status pa_get_block_table(const pa_allocator* a, int64_t seq_id, int32_t* out, int32_t cap,
+                             int32_t* len, int32_t* seq_len);
+
+/* Padded tables for a batch: tables_out [num_seqs][max_blocks] (-1 padding),
+ * lens_out [num_seqs] (either may be NULL). */
+pa_status pa_pack_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                               int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
+
+int32_t pa_num_free_blocks(const pa_allocator* a);
+int32_t pa_block_refcount(const pa_allocator* a, int32_t block);
+
+/* Counters: [0] blocks in use, [1] blocks shared (refcount > 1), [2] copies
+ * made by copy-on-write, [3] OOM refusals, [4] live sequences. */
+pa_status pa_allocator_stats(const pa_allocator* a, int64_t* out5);
+
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

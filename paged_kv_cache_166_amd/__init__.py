@@ -1,0 +1,346 @@
+"""Python binding of libpa.so: paged attention for AMD Instinct MI355X (gfx950).
+
+Argument marshalling only.  Every step of the hot path runs in the library's
+HIP kernels or its C++ allocator; torch supplies device memory and streams.
+The names follow the C ABI in ``include/pa.h``:
+
+* ``pa_reshape_and_cache`` -- scatter new K/V rows into pool slots;
+* ``pa_copy_blocks``       -- whole-block copies for copy-on-write;
+* ``pa_decode``            -- one query token per sequence over its paged K/V;
+* ``pa_prefill_chunk``     -- causal attention of a query chunk over its
+  paged context;
+* ``Allocator``            -- the host block allocator (free list, block
+  tables, slot mapping, fork / copy-on-write, OOM).
+
+Importing this module loads ``libpa.so`` from the package directory and fails
+loudly if it is missing: there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_SEQ = 0, -1, -2, -3, -4, -5
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+
+_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+          torch.float8_e4m3fn: PA_FP8_E4M3}
+_NAME = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "fp8": torch.float8_e4m3fn}
+
+# Every symbol the header declares; checked at load time.
+EXPORTS = [
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_auto_partition_blocks",
+    "pa_decode_workspace_bytes", "pa_decode_workspace_init", "pa_decode", "pa_prefill_chunk",
+    "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_prompt", "pa_append_tokens",
+    "pa_append_tokens_batch", "pa_fork", "pa_free_seq", "pa_get_block_table",
+    "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
+    "pa_last_error",
+]
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                          "(or python paged_kv_cache_166_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    missing = [s for s in EXPORTS if not hasattr(lib, s)]
+    if missing:
+        raise ImportError(f"libpa.so lacks {missing}")
+    P, I32, I64, SZ, VP = (ctypes.POINTER(_Pool), ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                           ctypes.c_void_p)
+    pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "pa_reshape_and_cache": (I32, [P, VP, VP, I32, VP, I32, VP]),
+        "pa_copy_blocks": (I32, [P, VP, I32, VP]),
+        "pa_decode_auto_partition_blocks": (I32, [P, I32, I32]),
+        "pa_decode_workspace_bytes": (SZ, [P, I32, I32, I32]),
+        "pa_decode_workspace_init": (I32, [VP, SZ, VP]),
+        "pa_decode": (I32, [VP, I32, VP, I32, P, VP, I32, VP, I32, ctypes.c_float, I32, VP, SZ, VP]),
+        "pa_prefill_chunk": (I32, [VP, I32, VP, I32, P, VP, I32, VP, VP, I32, I32, ctypes.c_float,
+                                   VP]),
+        "pa_allocator_create": (I32, [I32, I32, pi32, ctypes.POINTER(VP)]),
+        "pa_allocator_destroy": (None, [VP]),
+        "pa_alloc_prompt": (I32, [VP, I64, I32, pi64]),
+        "pa_append_tokens": (I32, [VP, I64, I32, pi64, pi32, pi32]),
+        "pa_append_tokens_batch": (I32, [VP, pi64, I32, I32, pi64, pi32, pi32]),
+        "pa_fork": (I32, [VP, I64, I64]),
+        "pa_free_seq": (I32, [VP, I64]),
+        "pa_get_block_table": (I32, [VP, I64, pi32, I32, pi32, pi32]),
+        "pa_pack_block_tables": (I32, [VP, pi64, I32, I32, pi32, pi32]),
+        "pa_num_free_blocks": (I32, [VP]),
+        "pa_block_refcount": (I32, [VP, I32]),
+        "pa_allocator_stats": (I32, [VP, pi64]),
+        "pa_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status, what):
+    if status == PA_OK:
+        return
+    msg = (lib.pa_last_error() or b"").decode()
+    if status == PA_ERR_OOM:
+        raise RuntimeError(msg if "OOM" in msg else f"OOM: {msg}")
+    if status == PA_ERR_INVALID:
+        raise ValueError(f"{what}: {msg}")
+    if status == PA_ERR_UNSUPPORTED:
+        raise NotImplementedError(f"{what}: {msg}")
+    if status == PA_ERR_NO_SEQ:
+        raise KeyError(f"{what}: {msg}")
+    raise RuntimeError(f"{what}: status {status}: {msg}")
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def dtype_code(x):
+    if isinstance(x, str):
+        return _NAME[x]
+    if isinstance(x, torch.dtype):
+        return _DTYPE[x]
+    return _DTYPE[x.dtype]
+
+
+# --------------------------------------------------------------------- pool
+
+class PagedPool:
+    """One layer's K/V pool: [num_blocks, num_heads, block_size, head_dim] each.
+
+    fp8 pools hold the codes as torch.float8_e4m3fn (or uint8) and one float32
+    scale per (block, head) for K and for V.
+    """
+
+    def __init__(self, k_cache, v_cache, k_scale=None, v_scale=None, kv_dtype=None):
+        assert k_cache.shape == v_cache.shape and k_cache.dim() == 4
+        assert k_cache.is_contiguous() and v_cache.is_contiguous()
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.k_scale, self.v_scale = k_scale, v_scale
+        N, H, bs, D = k_cache.shape
+        self.num_blocks, self.num_heads, self.block_size, self.head_dim = N, H, bs, D
+        if kv_dtype is None:
+            kv_dtype = PA_FP8_E4M3 if k_cache.dtype == torch.uint8 else dtype_code(k_cache)
+        self.kv_dtype = kv_dtype
+        self._struct = _Pool(k_cache.data_ptr(), v_cache.data_ptr(),
+                             k_scale.data_ptr() if k_scale is not None else 0,
+                             v_scale.data_ptr() if v_scale is not None else 0,
+                             N, H, bs, D, kv_dtype)
+
+    @property
+    def device(self):
+        return self.k_cache.device
+
+    def ref(self):
+        return ctypes.byref(self._struct)
+
+    @staticmethod
+    def empty(num_blocks, num_heads, block_size, head_dim, kv_dtype, device, fill=None):
+        """Allocate a pool (and fp8 scales of 1.0)."""
+        tdt = torch.uint8 if kv_dtype == "fp8" else TORCH_DTYPE[kv_dtype]
+        shape = (num_blocks, num_heads, block_size, head_dim)
+        k = torch.empty(shape, dtype=tdt, device=device)
+        v = torch.empty(shape, dtype=tdt, device=device)
+        if fill is not None:
+            k.fill_(fill)
+            v.fill_(fill)
+        ks = vs = None
+        if kv_dtype == "fp8":
+            ks = torch.ones((num_blocks, num_heads), dtype=torch.float32, device=device)
+            vs = torch.ones((num_blocks, num_heads), dtype=torch.float32, device=device)
+        return PagedPool(k, v, ks, vs, _NAME[kv_dtype])
+
+
+# ---------------------------------------------------------------- GPU calls
+
+def pa_reshape_and_cache(pool, key, value, slot_mapping, stream=None):
+    """key/value [T, H, D] (contiguous), slot_mapping [T] int64 on the device."""
+    assert key.is_contiguous() and value.is_contiguous() and slot_mapping.dtype == torch.int64
+    T = key.shape[0]
+    _check(lib.pa_reshape_and_cache(pool.ref(), _ptr(key), _ptr(value), dtype_code(key),
+                                    _ptr(slot_mapping), T, _stream(stream, pool.device)),
+           "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(pool, src_dst, stream=None):
+    """src_dst [n, 2] int32 on the device."""
+    assert src_dst.dtype == torch.int32 and src_dst.is_contiguous()
+    _check(lib.pa_copy_blocks(pool.ref(), _ptr(src_dst), src_dst.shape[0],
+                              _stream(stream, pool.device)), "pa_copy_blocks")
+
+
+def pa_decode_auto_partition_blocks(pool, num_seqs, max_blocks_per_seq):
+    return lib.pa_decode_auto_partition_blocks(pool.ref(), num_seqs, max_blocks_per_seq)
+
+
+def pa_decode_workspace_bytes(pool, num_seqs, max_blocks_per_seq, partition_blocks=0):
+    return lib.pa_decode_workspace_bytes(pool.ref(), num_seqs, max_blocks_per_seq, partition_blocks)
+
+
+def decode_workspace(pool, num_seqs, max_blocks_per_seq, partition_blocks=0, stream=None):
+    """A zero-initialised workspace tensor for pa_decode (or None if unneeded)."""
+    n = pa_decode_workspace_bytes(pool, num_seqs, max_blocks_per_seq, partition_blocks)
+    if n == 0:
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=pool.device)
+    _check(lib.pa_decode_workspace_init(_ptr(ws), n, _stream(stream, pool.device)),
+           "pa_decode_workspace_init")
+    return ws
+
+
+def pa_decode(out, q, pool, block_tables, context_lens, scale, partition_blocks=0,
+              workspace=None, stream=None, q_dtype=None, out_dtype=None):
+    """out/q [B, H, D]; block_tables [B, max_blocks] int32; context_lens [B] int32."""
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert block_tables.is_contiguous() and q.is_contiguous() and out.is_contiguous()
+    B, maxb = block_tables.shape
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib.pa_decode(_ptr(out), dtype_code(out) if out_dtype is None else out_dtype,
+                         _ptr(q), dtype_code(q) if q_dtype is None else q_dtype, pool.ref(),
+                         _ptr(block_tables), maxb, _ptr(context_lens), B, float(scale),
+                         int(partition_blocks), _ptr(workspace), ws_bytes,
+                         _stream(stream, pool.device)), "pa_decode")
+
+
+def pa_prefill_chunk(out, q, pool, block_tables, context_lens, query_start_loc, max_query_len,
+                     scale, stream=None):
+    """out/q packed [T, H, D]; query_start_loc [B+1] int32; context_lens [B] int32."""
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert query_start_loc.dtype == torch.int32
+    B, maxb = block_tables.shape
+    _check(lib.pa_prefill_chunk(_ptr(out), dtype_code(out), _ptr(q), dtype_code(q), pool.ref(),
+                                _ptr(block_tables), maxb, _ptr(context_lens),
+                                _ptr(query_start_loc), B, int(max_query_len), float(scale),
+                                _stream(stream, pool.device)), "pa_prefill_chunk")
+
+
+# ------------------------------------------------------------ host allocator
+
+def _i32p(arr):
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _i64p(arr):
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+class Allocator:
+    """Host block allocator (C++): FIFO free list, refcounted blocks,
+    copy-on-write, all-or-nothing operations.  OOM raises RuntimeError("OOM")."""
+
+    def __init__(self, num_blocks, block_size, free_order=None):
+        import numpy as np
+        self._np = np
+        h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+        _check(lib.pa_allocator_create(num_blocks, block_size,
+                                       _i32p(order) if order is not None else None,
+                                       ctypes.byref(h)), "pa_allocator_create")
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def __del__(self, _destroy=lib.pa_allocator_destroy):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _destroy(h)
+            self._h = None
+
+    def alloc_prompt(self, seq_id, num_tokens):
+        slots = self._np.empty(num_tokens, dtype=self._np.int64)
+        _check(lib.pa_alloc_prompt(self._h, seq_id, num_tokens, _i64p(slots)), "pa_alloc_prompt")
+        return slots
+
+    def append_tokens(self, seq_id, n=1):
+        """Returns (slots, cow) with cow = (src, dst) or None."""
+        np = self._np
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        pair = np.empty(2, dtype=np.int32)
+        ncow = np.zeros(1, dtype=np.int32)
+        _check(lib.pa_append_tokens(self._h, seq_id, n, _i64p(slots), _i32p(pair), _i32p(ncow)),
+               "pa_append_tokens")
+        return slots[:n], ((int(pair[0]), int(pair[1])) if ncow[0] else None)
+
+    def append_tokens_batch(self, seq_ids, n=1, slots_out=None, cow_out=None):
+        """Append n tokens to each sequence; returns (slots [B, n], cow_pairs [B, 2], num_cow)."""
+        np = self._np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        B = ids.shape[0]
+        slots = slots_out if slots_out is not None else np.empty((B, n), dtype=np.int64)
+        cow = cow_out if cow_out is not None else np.empty((B, 2), dtype=np.int32)
+        ncow = np.zeros(1, dtype=np.int32)
+        _check(lib.pa_append_tokens_batch(self._h, _i64p(ids), B, n, _i64p(slots), _i32p(cow),
+                                          _i32p(ncow)), "pa_append_tokens_batch")
+        return slots, cow, int(ncow[0])
+
+    def fork(self, parent_id, child_id):
+        _check(lib.pa_fork(self._h, parent_id, child_id), "pa_fork")
+
+    def free_seq(self, seq_id):
+        _check(lib.pa_free_seq(self._h, seq_id), "pa_free_seq")
+
+    def block_table(self, seq_id):
+        np = self._np
+        n = ctypes.c_int32()
+        _check(lib.pa_get_block_table(self._h, seq_id, None, 0, ctypes.byref(n), None),
+               "pa_get_block_table")
+        out = np.empty(max(n.value, 1), dtype=np.int32)
+        _check(lib.pa_get_block_table(self._h, seq_id, _i32p(out), n.value, None, None),
+               "pa_get_block_table")
+        return [int(x) for x in out[: n.value]]
+
+    def seq_len(self, seq_id):
+        n = ctypes.c_int32()
+        _check(lib.pa_get_block_table(self._h, seq_id, None, 0, None, ctypes.byref(n)),
+               "pa_get_block_table")
+        return n.value
+
+    def pack(self, seq_ids, max_blocks, tables_out=None, lens_out=None):
+        """Padded int32 tables [B, max_blocks] (-1 padding) and lengths [B]."""
+        np = self._np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        B = ids.shape[0]
+        t = tables_out if tables_out is not None else np.empty((B, max_blocks), dtype=np.int32)
+        ln = lens_out if lens_out is not None else np.empty(B, dtype=np.int32)
+        _check(lib.pa_pack_block_tables(self._h, _i64p(ids), B, max_blocks, _i32p(t), _i32p(ln)),
+               "pa_pack_block_tables")
+        return t, ln
+
+    def num_free(self):
+        return lib.pa_num_free_blocks(self._h)
+
+    def refcount(self, block):
+        return lib.pa_block_refcount(self._h, block)
+
+    def stats(self):
+        np = self._np
+        out = np.zeros(5, dtype=np.int64)
+        _check(lib.pa_allocator_stats(self._h, _i64p(out)), "pa_allocator_stats")
+        return dict(used=int(out[0]), shared=int(out[1]), cow_copies=int(out[2]),
+                    oom=int(out[3]), seqs=int(out[4]))

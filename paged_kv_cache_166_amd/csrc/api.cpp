@@ -1,0 +1,232 @@
+// C ABI of the GPU calls in pa.h: argument checks, then one launch each.
+// Nothing is launched when a check fails.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "pa.h"
+#include "status.h"
+
+namespace {
+
+using pa::fail;
+
+bool valid_dtype(int32_t dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
+bool valid_io_dtype(int32_t dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int elem_bytes(int32_t dt) { return dt == PA_F32 ? 4 : (dt == PA_FP8_E4M3 ? 1 : 2); }
+
+pa_status check_pool(const char* fn, const pa_pool* p) {
+  if (!p) return fail(PA_ERR_INVALID, "%s: pool is NULL", fn);
+  if (!p->k_cache || !p->v_cache) return fail(PA_ERR_INVALID, "%s: NULL cache pointer", fn);
+  if (!aligned(p->k_cache, 128) || !aligned(p->v_cache, 128))
+    return fail(PA_ERR_INVALID, "%s: cache bases must be 128-byte aligned", fn);
+  if (p->num_blocks <= 0 || p->num_heads <= 0 || p->num_heads > 65535)
+    return fail(PA_ERR_INVALID, "%s: num_blocks=%d num_heads=%d", fn, p->num_blocks, p->num_heads);
+  if (p->block_size != 4 && p->block_size != 8 && p->block_size != 16 && p->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (built: 4, 8, 16, 32)", fn, p->block_size);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", fn, p->head_dim);
+  if (!valid_dtype(p->kv_dtype)) return fail(PA_ERR_INVALID, "%s: kv_dtype %d", fn, p->kv_dtype);
+  if (p->kv_dtype == PA_FP8_E4M3) {
+    if (!p->k_scale || !p->v_scale) return fail(PA_ERR_INVALID, "%s: fp8 pool without scales", fn);
+  }
+  return PA_OK;
+}
+
+pa_status hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return PA_OK;
+}
+
+int32_t auto_partition_blocks(const pa_pool* p) {
+  int32_t b = 256 / p->block_size;
+  return b < 1 ? 1 : (b > 64 ? 64 : b);
+}
+
+struct WsLayout {
+  int64_t cnt_off, ml_off, acc_off, bytes;
+  int32_t parts;
+};
+
+WsLayout ws_layout(const pa_pool* p, int32_t num_seqs, int32_t max_blocks, int32_t part_blocks) {
+  WsLayout w{};
+  w.parts = (max_blocks + part_blocks - 1) / part_blocks;
+  if (w.parts <= 1) return w;
+  const int64_t sh = int64_t(num_seqs) * p->num_heads;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  w.cnt_off = 0;
+  w.ml_off = up(sh * 4);
+  w.acc_off = w.ml_off + up(sh * w.parts * 2 * 4);
+  w.bytes = w.acc_off + up(sh * w.parts * p->head_dim * 4);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const pa_pool* pool, const void* key, const void* value,
+                               int32_t in_dtype, const int64_t* slot_mapping,
+                               int32_t num_tokens, hipStream_t stream) {
+  const char* fn = "pa_reshape_and_cache";
+  if (pa_status s = check_pool(fn, pool)) return s;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "%s: num_tokens < 0", fn);
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID, "%s: key/value must be 16-byte aligned", fn);
+  if (pool->kv_dtype == PA_FP8_E4M3) {
+    if (!valid_io_dtype(in_dtype))
+      return fail(PA_ERR_INVALID, "%s: fp8 pool takes f32/f16/bf16 rows, got %d", fn, in_dtype);
+  } else if (in_dtype != pool->kv_dtype) {
+    return fail(PA_ERR_INVALID, "%s: in_dtype %d must equal kv_dtype %d", fn, in_dtype,
+                pool->kv_dtype);
+  }
+  pa::CacheWriteArgs a{pool->k_cache, pool->v_cache, pool->k_scale, pool->v_scale,
+                       key,           value,         slot_mapping,  num_tokens,
+                       pool->num_heads, pool->block_size, pool->head_dim, in_dtype,
+                       pool->kv_dtype};
+  return hip_status(fn, pa::launch_reshape_and_cache(a, stream));
+}
+
+pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t num_pairs,
+                         hipStream_t stream) {
+  const char* fn = "pa_copy_blocks";
+  if (pa_status s = check_pool(fn, pool)) return s;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "%s: num_pairs < 0", fn);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst) return fail(PA_ERR_INVALID, "%s: src_dst is NULL", fn);
+  const bool fp8 = pool->kv_dtype == PA_FP8_E4M3;
+  pa::CopyBlocksArgs a{pool->k_cache,
+                       pool->v_cache,
+                       fp8 ? pool->k_scale : nullptr,
+                       fp8 ? pool->v_scale : nullptr,
+                       src_dst,
+                       num_pairs,
+                       pool->num_heads,
+                       int64_t(pool->block_size) * pool->head_dim * elem_bytes(pool->kv_dtype)};
+  return hip_status(fn, pa::launch_copy_blocks(a, stream));
+}
+
+int32_t pa_decode_auto_partition_blocks(const pa_pool* pool, int32_t num_seqs,
+                                        int32_t max_blocks_per_seq) {
+  (void)num_seqs;
+  (void)max_blocks_per_seq;
+  if (check_pool("pa_decode_auto_partition_blocks", pool)) return -1;
+  return auto_partition_blocks(pool);
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, int32_t partition_blocks) {
+  if (check_pool("pa_decode_workspace_bytes", pool)) return 0;
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0) return 0;
+  const int32_t pb = partition_blocks > 0 ? partition_blocks : auto_partition_blocks(pool);
+  return size_t(ws_layout(pool, num_seqs, max_blocks_per_seq, pb).bytes);
+}
+
+pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (!workspace || !aligned(workspace, 256))
+    return fail(PA_ERR_INVALID, "pa_decode_workspace_init: workspace must be 256-byte aligned");
+  return hip_status("pa_decode_workspace_init",
+                    pa::launch_zero_i32(static_cast<int32_t*>(workspace),
+                                        int64_t(workspace_bytes / 4), stream));
+}
+
+pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                    const pa_pool* pool, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    float scale, int32_t partition_blocks, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "pa_decode";
+  if (pa_status s = check_pool(fn, pool)) return s;
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "%s: num_seqs %d", fn, num_seqs);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(q, 16) || !aligned(out, 16))
+    return fail(PA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq <= 0", fn);
+  if (pool->kv_dtype == PA_FP8_E4M3) {
+    if (!valid_io_dtype(q_dtype)) return fail(PA_ERR_INVALID, "%s: q_dtype %d", fn, q_dtype);
+  } else if (q_dtype != pool->kv_dtype) {
+    return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype %d must equal kv_dtype %d", fn, q_dtype,
+                pool->kv_dtype);
+  }
+  if (out_dtype != PA_F32 && out_dtype != q_dtype)
+    return fail(PA_ERR_INVALID, "%s: out_dtype must be f32 or q_dtype", fn);
+  if (partition_blocks < 0 || partition_blocks > 64)
+    return fail(PA_ERR_UNSUPPORTED, "%s: partition_blocks %d (1..64, or 0 = auto)", fn,
+                partition_blocks);
+  const int32_t pb = partition_blocks > 0 ? partition_blocks : auto_partition_blocks(pool);
+  const WsLayout w = ws_layout(pool, num_seqs, max_blocks_per_seq, pb);
+  if (w.parts > 1) {
+    if (!workspace || size_t(w.bytes) > workspace_bytes || !aligned(workspace, 256))
+      return fail(PA_ERR_INVALID, "%s: workspace of %lld bytes, 256-byte aligned, is required",
+                  fn, (long long)w.bytes);
+  }
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_cnt = w.parts > 1 ? reinterpret_cast<int32_t*>(ws + w.cnt_off) : nullptr;
+  a.ws_ml = w.parts > 1 ? reinterpret_cast<float*>(ws + w.ml_off) : nullptr;
+  a.ws_acc = w.parts > 1 ? reinterpret_cast<float*>(ws + w.acc_off) : nullptr;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = pool->num_heads;
+  a.part_blocks = pb;
+  a.max_parts = w.parts < 1 ? 1 : w.parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.q_dtype = q_dtype;
+  a.out_dtype = out_dtype;
+  return hip_status(fn, pa::launch_decode(a, pool->kv_dtype, pool->head_dim, pool->block_size,
+                                          num_seqs, stream));
+}
+
+pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                           const pa_pool* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs,
+                           int32_t max_query_len, float scale, hipStream_t stream) {
+  const char* fn = "pa_prefill_chunk";
+  if (pa_status s = check_pool(fn, pool)) return s;
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "%s: num_seqs %d", fn, num_seqs);
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (max_query_len < 0) return fail(PA_ERR_INVALID, "%s: max_query_len < 0", fn);
+  if (!out || !q || !block_tables || !context_lens || !query_start_loc)
+    return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(q, 16) || !aligned(out, 16))
+    return fail(PA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq <= 0", fn);
+  if (pool->kv_dtype != PA_F16 && pool->kv_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: kv_dtype %d (built: f16, bf16)", fn, pool->kv_dtype);
+  if (q_dtype != pool->kv_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype must equal kv_dtype", fn);
+  if (out_dtype != PA_F32 && out_dtype != q_dtype)
+    return fail(PA_ERR_INVALID, "%s: out_dtype must be f32 or q_dtype", fn);
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = pool->num_heads;
+  a.num_seqs = num_seqs;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_dtype = out_dtype;
+  return hip_status(fn, pa::launch_prefill(a, pool->kv_dtype, pool->head_dim, pool->block_size,
+                                           max_query_len, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,423 @@
+// pa_decode: one query token per sequence against its paged K/V, on gfx950.
+//
+// What is computed (blog article section 3.2.2 forward pass at a single query
+// row; vLLM course ch. 4 attention pseudocode): for each sequence i and head
+// h, softmax(scale * q K^T) V over the L_i cached tokens, with K and V read
+// block by block through the sequence's block table.
+//
+// How (decode is a gather-GEMV: ~1 flop per byte, so HBM bandwidth bounds it
+// and MFMA has nothing to do here):
+//  * grid (partition, head, sequence); a workgroup of NW wavefronts owns one
+//    partition of `part_blocks` blocks of one (sequence, head); wave w takes
+//    blocks w, w+NW, ... of the partition;
+//  * the partition's block-table entries are read once into a VGPR (lane t
+//    holds entry t) and each block id is moved to an SGPR with readlane, so
+//    every tile address is scalar;
+//  * one (block, head) tile is contiguous in the [N][H][bs][D] pool; a
+//    wave-wide 16-byte-per-lane load covers 1 KiB of it, so K and V tiles are
+//    read with fully coalesced dwordx4 loads straight into registers (each
+//    lane consumes exactly the bytes it loads, so staging through LDS would
+//    only add traffic);
+//  * lanes form groups of `lanes per row` (16 for a 128 x 16-bit row): a
+//    group holds one key/value row per load, the q.k partial sums are reduced
+//    inside the group with DPP, and each group keeps its own running max and
+//    sum (online softmax) over the rows it sees -- no cross-group traffic in
+//    the loop;
+//  * the next block's K and V loads are issued before the current block is
+//    consumed (two register buffers);
+//  * at the end the groups, then the waves, merge their (max, sum, acc)
+//    triples; a partition writes its triple to the workspace and the last
+//    partition of a (sequence, head) to finish (an atomic counter) merges all
+//    of them and writes the output, so split-K needs no second kernel.
+// Scores live in the log2 domain: s = log2(e) * scale * q.k, p = exp2(s - m).
+#include "device.h"
+#include "kernels.h"
+
+namespace pa {
+namespace {
+
+template <int KV, int D, int BS>
+struct Geo {
+  static constexpr int kElem = dtype_bytes(KV);
+  static constexpr int kRowBytes = D * kElem;
+  static constexpr int kLpr = kRowBytes / 16;        // lanes per K/V row
+  static constexpr int kEpl = 16 / kElem;            // elements per lane per load
+  static constexpr int kRows = 64 / kLpr;            // rows one wave-load covers
+  static constexpr bool kIdleGroups = BS < kRows;    // groups past the block's rows
+  static constexpr int kLoads = kIdleGroups ? 1 : BS / kRows;
+  static constexpr int64_t kTileBytes = int64_t(BS) * kRowBytes;
+  static_assert(kLpr >= 4 && kLpr <= 32, "row must span 4..32 lanes");
+};
+
+template <int KV>
+struct KvOps;
+
+template <>
+struct KvOps<PA_F32> {
+  static constexpr int kEpl = 4;
+  struct Q { float v[4]; };
+  __device__ static Q load_q(const void* q, int64_t off, int) {
+    float4 x = *(const float4*)((const float*)q + off);
+    return Q{{x.x, x.y, x.z, x.w}};
+  }
+  __device__ static float dot(const Q& q, uint4 k) {
+    float s = q.v[0] * __uint_as_float(k.x);
+    s = fmaf(q.v[1], __uint_as_float(k.y), s);
+    s = fmaf(q.v[2], __uint_as_float(k.z), s);
+    return fmaf(q.v[3], __uint_as_float(k.w), s);
+  }
+  __device__ static void axpy(float* acc, float p, uint4 v) {
+    acc[0] = fmaf(p, __uint_as_float(v.x), acc[0]);
+    acc[1] = fmaf(p, __uint_as_float(v.y), acc[1]);
+    acc[2] = fmaf(p, __uint_as_float(v.z), acc[2]);
+    acc[3] = fmaf(p, __uint_as_float(v.w), acc[3]);
+  }
+};
+
+template <>
+struct KvOps<PA_F16> {
+  static constexpr int kEpl = 8;
+  struct Q { uint4 raw; };  // q in the pool's format: exact products in v_dot2
+  __device__ static Q load_q(const void* q, int64_t off, int) {
+    return Q{*(const uint4*)((const uint16_t*)q + off)};
+  }
+  __device__ static float dot(const Q& q, uint4 k) {
+    float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.raw.x),
+                                     __builtin_bit_cast(half2_t, k.x), 0.f, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.raw.y),
+                               __builtin_bit_cast(half2_t, k.y), s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.raw.z),
+                               __builtin_bit_cast(half2_t, k.z), s, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.raw.w),
+                                  __builtin_bit_cast(half2_t, k.w), s, false);
+  }
+  __device__ static void axpy(float* acc, float p, uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(p, f16_lo(w[i]), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(p, f16_hi(w[i]), acc[2 * i + 1]);
+    }
+  }
+};
+
+template <>
+struct KvOps<PA_BF16> {
+  static constexpr int kEpl = 8;
+  struct Q { uint4 raw; };
+  __device__ static Q load_q(const void* q, int64_t off, int) {
+    return Q{*(const uint4*)((const uint16_t*)q + off)};
+  }
+  __device__ static float dot(const Q& q, uint4 k) {
+    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.raw.x),
+                                              __builtin_bit_cast(bf162_t, k.x), 0.f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.raw.y),
+                                        __builtin_bit_cast(bf162_t, k.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.raw.z),
+                                        __builtin_bit_cast(bf162_t, k.z), s, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.raw.w),
+                                           __builtin_bit_cast(bf162_t, k.w), s, false);
+  }
+  __device__ static void axpy(float* acc, float p, uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(p, bf16_lo(w[i]), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(p, bf16_hi(w[i]), acc[2 * i + 1]);
+    }
+  }
+};
+
+template <>
+struct KvOps<PA_FP8_E4M3> {
+  static constexpr int kEpl = 16;
+  struct Q { float v[16]; };  // q converted to float32 once
+  __device__ static Q load_q(const void* q, int64_t off, int q_dtype) {
+    Q r;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r.v[e] = load_as_f32(q, off + e, q_dtype);
+    return r;
+  }
+  __device__ static float dot(const Q& q, uint4 k) {
+    const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float2_t a = fp8x2_lo(w[i]);
+      float2_t b = fp8x2_hi(w[i]);
+      s = fmaf(q.v[4 * i], a.x, s);
+      s = fmaf(q.v[4 * i + 1], a.y, s);
+      s = fmaf(q.v[4 * i + 2], b.x, s);
+      s = fmaf(q.v[4 * i + 3], b.y, s);
+    }
+    return s;
+  }
+  __device__ static void axpy(float* acc, float p, uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float2_t a = fp8x2_lo(w[i]);
+      float2_t b = fp8x2_hi(w[i]);
+      acc[4 * i] = fmaf(p, a.x, acc[4 * i]);
+      acc[4 * i + 1] = fmaf(p, a.y, acc[4 * i + 1]);
+      acc[4 * i + 2] = fmaf(p, b.x, acc[4 * i + 2]);
+      acc[4 * i + 3] = fmaf(p, b.y, acc[4 * i + 3]);
+    }
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int KV, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+  using G = Geo<KV, D, BS>;
+  using Ops = KvOps<KV>;
+  constexpr int E = G::kEpl;
+  static_assert(E == Ops::kEpl, "lane element count");
+
+  const int part = blockIdx.x;
+  const int head = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int H = a.num_heads;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int L = a.context_lens[seq];
+  const int64_t out_off = (int64_t(seq) * H + head) * D;
+  if (L <= 0) {
+    if (part == 0)
+      for (int d = tid; d < D; d += NW * 64) store_from_f32(a.out, out_off + d, a.out_dtype, 0.f);
+    return;
+  }
+  const int nblocks = (L + BS - 1) / BS;
+  const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
+  if (part >= nparts) return;
+  const int blk0 = part * a.part_blocks;
+  const int nb = min(a.part_blocks, nblocks - blk0);
+
+  const int grp = lane / G::kLpr;
+  const int col = lane % G::kLpr;
+  const bool row_ok = !G::kIdleGroups || grp < BS;
+
+  // Block ids of this partition: lane t holds entry blk0 + t.
+  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq + blk0;
+  const int tab = lane < nb ? table[lane] : 0;
+
+  const typename Ops::Q q = Ops::load_q(a.q, out_off + col * E, a.q_dtype);
+  const int64_t blk_stride = int64_t(H) * G::kTileBytes;
+  const char* kbase = (const char*)a.k_cache + int64_t(head) * G::kTileBytes + lane * 16;
+  const char* vbase = (const char*)a.v_cache + int64_t(head) * G::kTileBytes + lane * 16;
+
+  float m = kNoMax, l = 0.f;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+
+  uint4 k0[G::kLoads], v0[G::kLoads], k1[G::kLoads], v1[G::kLoads];
+  int p0 = 0, p1 = 0;
+
+  auto issue = [&](uint4* kr, uint4* vr, int& phys, int jl) {
+    phys = __builtin_amdgcn_readlane(tab, jl);
+    const char* kp = kbase + int64_t(phys) * blk_stride;
+    const char* vp = vbase + int64_t(phys) * blk_stride;
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      if (row_ok) {
+        kr[i] = *(const uint4*)(kp + i * 1024);
+        vr[i] = *(const uint4*)(vp + i * 1024);
+      } else {
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  auto consume = [&](uint4* kr, uint4* vr, int phys, int jl) {
+    float mul_k = a.scale_log2;
+    float mul_v = 1.f;
+    if constexpr (KV == PA_FP8_E4M3) {
+      mul_k *= a.k_scale[int64_t(phys) * H + head];
+      mul_v = a.v_scale[int64_t(phys) * H + head];
+    }
+    const int tok0 = (blk0 + jl) * BS + grp;  // token of load 0 in this lane's group
+    const bool full = (blk0 + jl + 1) * BS <= L;
+    float s[G::kLoads];
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      s[i] = group_sum<G::kLpr>(Ops::dot(q, kr[i])) * mul_k;
+      if constexpr (G::kIdleGroups) s[i] = row_ok ? s[i] : -INFINITY;
+    }
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < G::kLoads; ++i) {
+        if (tok0 + i * G::kRows >= L) {
+          s[i] = -INFINITY;
+          vr[i] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) mx = fmaxf(mx, s[i]);
+    const float alpha = fast_exp2(m - mx);
+    float psum = 0.f;
+    float p[G::kLoads];
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      p[i] = fast_exp2(s[i] - mx);
+      psum += p[i];
+    }
+    l = fmaf(l, alpha, psum);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) Ops::axpy(acc, p[i] * mul_v, vr[i]);
+    m = mx;
+  };
+
+  // Two-deep software pipeline over this wave's blocks wave, wave+NW, ...
+  int jl = wave;
+  if (jl < nb) issue(k0, v0, p0, jl);
+  while (jl < nb) {
+    int jn = jl + NW;
+    if (jn < nb) issue(k1, v1, p1, jn);
+    consume(k0, v0, p0, jl);
+    jl = jn;
+    if (jl >= nb) break;
+    jn = jl + NW;
+    if (jn < nb) issue(k0, v0, p0, jn);
+    consume(k1, v1, p1, jl);
+    jl = jn;
+  }
+
+  // Merge the groups of this wave (lanes with equal col, different grp).
+#pragma unroll
+  for (int mask = G::kLpr; mask < 64; mask <<= 1) {
+    const float mo = __shfl_xor(m, mask);
+    const float lo = __shfl_xor(l, mask);
+    const float mx = fmaxf(m, mo);
+    const float sa = fast_exp2(m - mx);
+    const float sb = fast_exp2(mo - mx);
+    l = l * sa + lo * sb;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = acc[e] * sa + __shfl_xor(acc[e], mask) * sb;
+    m = mx;
+  }
+
+  // Merge the waves through LDS.
+  __shared__ float sm_acc[NW][D];
+  __shared__ float sm_m[NW], sm_l[NW];
+  __shared__ int s_last;
+  if (lane < G::kLpr) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) sm_acc[wave][col * E + e] = acc[e];
+  }
+  if (lane == 0) {
+    sm_m[wave] = m;
+    sm_l[wave] = l;
+  }
+  __syncthreads();
+
+  float A = 0.f, M = kNoMax, S = 0.f;
+  if (tid < D) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(sm_m[w] - M);
+      S = fmaf(sm_l[w], f, S);
+      A = fmaf(sm_acc[w][tid], f, A);
+    }
+  }
+
+  if (nparts == 1) {
+    if (tid < D) store_from_f32(a.out, out_off + tid, a.out_dtype, S > 0.f ? A / S : 0.f);
+    return;
+  }
+
+  // Split-K: publish this partition's triple, the last one merges.
+  const int64_t sh = int64_t(seq) * H + head;
+  const int64_t pidx = sh * a.max_parts + part;
+  if (tid < D) a.ws_acc[pidx * D + tid] = A;
+  if (tid == 0) {
+    a.ws_ml[2 * pidx] = M;
+    a.ws_ml[2 * pidx + 1] = S;
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.ws_cnt[sh], 1) == nparts - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (tid < D) {
+    const float* ml = a.ws_ml + 2 * sh * a.max_parts;
+    const float* pa = a.ws_acc + sh * a.max_parts * D + tid;
+    float Mg = kNoMax;
+    for (int p = 0; p < nparts; ++p) Mg = fmaxf(Mg, ml[2 * p]);
+    float Ag = 0.f, Sg = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+      const float f = fast_exp2(ml[2 * p] - Mg);
+      Sg = fmaf(ml[2 * p + 1], f, Sg);
+      Ag = fmaf(pa[int64_t(p) * D], f, Ag);
+    }
+    store_from_f32(a.out, out_off + tid, a.out_dtype, Sg > 0.f ? Ag / Sg : 0.f);
+  }
+  if (tid == 0) atomicExch(&a.ws_cnt[sh], 0);
+}
+
+__global__ void zero_i32_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
+constexpr int kWaves = 4;
+
+template <int KV, int D, int BS>
+hipError_t launch_t(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
+  dim3 grid(a.max_parts, a.num_heads, num_seqs);
+  hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int KV, int D>
+hipError_t launch_bs(const DecodeArgs& a, int bs, int num_seqs, hipStream_t stream) {
+  switch (bs) {
+    case 4: return launch_t<KV, D, 4>(a, num_seqs, stream);
+    case 8: return launch_t<KV, D, 8>(a, num_seqs, stream);
+    case 16: return launch_t<KV, D, 16>(a, num_seqs, stream);
+    case 32: return launch_t<KV, D, 32>(a, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int KV>
+hipError_t launch_d(const DecodeArgs& a, int d, int bs, int num_seqs, hipStream_t stream) {
+  if (d == 64) return launch_bs<KV, 64>(a, bs, num_seqs, stream);
+  if (d == 128) return launch_bs<KV, 128>(a, bs, num_seqs, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
+                         int num_seqs, hipStream_t stream) {
+  switch (kv_dtype) {
+    case PA_F32: return launch_d<PA_F32>(a, head_dim, block_size, num_seqs, stream);
+    case PA_F16: return launch_d<PA_F16>(a, head_dim, block_size, num_seqs, stream);
+    case PA_BF16: return launch_d<PA_BF16>(a, head_dim, block_size, num_seqs, stream);
+    case PA_FP8_E4M3: return launch_d<PA_FP8_E4M3>(a, head_dim, block_size, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int blocks = int((n + 255) / 256);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace pa

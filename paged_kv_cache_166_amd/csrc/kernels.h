@@ -1,0 +1,84 @@
+// Host-side view of the kernels: argument blocks and launchers (internal to
+// libpa.so; the public surface is include/pa.h).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_acc;    // [num_seqs][num_heads][max_parts][head_dim]
+  float* ws_ml;     // [num_seqs][num_heads][max_parts][2]  (max, sum)
+  int32_t* ws_cnt;  // [num_seqs][num_heads]
+  int32_t max_blocks_per_seq;
+  int32_t num_heads;
+  int32_t part_blocks;
+  int32_t max_parts;
+  float scale_log2;  // scale * log2(e)
+  int32_t q_dtype;
+  int32_t out_dtype;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
+                         int num_seqs, hipStream_t stream);
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
+
+struct CacheWriteArgs {
+  void* k_cache;
+  void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+  int32_t num_tokens;
+  int32_t num_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t in_dtype;
+  int32_t kv_dtype;
+};
+
+hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
+
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;
+  float* v_scale;
+  const int32_t* src_dst;
+  int32_t num_pairs;
+  int32_t num_heads;
+  int64_t tile_bytes;  // block_size * head_dim * element size
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  int32_t max_blocks_per_seq;
+  int32_t num_heads;
+  int32_t num_seqs;
+  float scale_log2;
+  int32_t out_dtype;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int block_size,
+                          int max_query_len, hipStream_t stream);
+
+}  // namespace pa

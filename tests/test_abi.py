@@ -1,0 +1,96 @@
+"""The C ABI: libpa.so loads without a GPU, exports every symbol the header
+declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_166_amd as pa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert "pa_decode" in names and "pa_prefill_chunk" in names and "pa_reshape_and_cache" in names
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(pa.EXPORTS) == names
+
+
+def _fake_pool(**kw):
+    f = dict(k_cache=0x10000, v_cache=0x20000, k_scale=0, v_scale=0, num_blocks=8, num_heads=2,
+             block_size=16, head_dim=128, kv_dtype=pa.PA_F16)
+    f.update(kw)
+    return pa._Pool(**f)
+
+
+def _decode(pool, **kw):
+    a = dict(out=0x30000, out_dtype=pa.PA_F32, q=0x40000, q_dtype=pa.PA_F16, tables=0x50000,
+             maxb=4, lens=0x60000, B=2, scale=0.1, pb=0, ws=0, wsb=0)
+    a.update(kw)
+    return pa.lib.pa_decode(ctypes.c_void_p(a["out"]), a["out_dtype"], ctypes.c_void_p(a["q"]),
+                            a["q_dtype"], ctypes.byref(pool), ctypes.c_void_p(a["tables"]), a["maxb"],
+                            ctypes.c_void_p(a["lens"]), a["B"], a["scale"], a["pb"],
+                            ctypes.c_void_p(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("block_size", 12, pa.PA_ERR_UNSUPPORTED),
+    ("head_dim", 96, pa.PA_ERR_UNSUPPORTED),
+    ("kv_dtype", 9, pa.PA_ERR_INVALID),
+    ("num_blocks", 0, pa.PA_ERR_INVALID),
+    ("k_cache", 0x10040, pa.PA_ERR_INVALID),      # not 128-byte aligned
+    ("k_cache", 0, pa.PA_ERR_INVALID),
+])
+def test_pool_checks(field, value, code):
+    assert _decode(_fake_pool(**{field: value})) == code
+    assert pa.lib.pa_last_error()
+
+
+def test_decode_argument_checks_before_launch():
+    p = _fake_pool()
+    assert _decode(p, q_dtype=pa.PA_BF16) == pa.PA_ERR_UNSUPPORTED     # q must match f16 pool
+    assert _decode(p, out_dtype=pa.PA_BF16) == pa.PA_ERR_INVALID       # out f32 or q dtype
+    assert _decode(p, q=0x40004) == pa.PA_ERR_INVALID                  # q alignment
+    assert _decode(p, pb=65) == pa.PA_ERR_UNSUPPORTED
+    assert _decode(p, B=0) == pa.PA_OK                                 # nothing to do
+    # 128 blocks at 16 per partition -> 8 partitions: a workspace is required
+    assert _decode(p, maxb=128, pb=16) == pa.PA_ERR_INVALID
+    need = pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 2, 128, 16)
+    assert need > 0
+    assert _decode(p, maxb=128, pb=16, ws=0x70000, wsb=need - 1) == pa.PA_ERR_INVALID
+    fp8 = _fake_pool(kv_dtype=pa.PA_FP8_E4M3)
+    assert _decode(fp8, q_dtype=pa.PA_BF16) == pa.PA_ERR_INVALID       # fp8 pool without scales
+
+
+def test_workspace_sizes():
+    p = _fake_pool()
+    assert pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 4, 16, 16) == 0   # one partition
+    b = pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 4, 33, 16)          # three partitions
+    # counters, (max, sum) and acc per (seq, head, partition), each 256-byte padded
+    assert b == 256 + 256 + ((4 * 2 * 3 * 128 * 4 + 255) // 256) * 256
+    assert pa.lib.pa_decode_auto_partition_blocks(ctypes.byref(p), 4, 33) == 16
+
+
+def test_reshape_and_prefill_checks():
+    p = _fake_pool()
+    r = pa.lib.pa_reshape_and_cache(ctypes.byref(p), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                                    pa.PA_BF16, ctypes.c_void_p(0x3000), 4, None)
+    assert r == pa.PA_ERR_INVALID                                       # in dtype != f16 pool
+    assert pa.lib.pa_reshape_and_cache(ctypes.byref(p), None, None, pa.PA_F16, None, 0, None) == pa.PA_OK
+    f32 = _fake_pool(kv_dtype=pa.PA_F32)
+    r = pa.lib.pa_prefill_chunk(ctypes.c_void_p(0x1000), pa.PA_F32, ctypes.c_void_p(0x2000), pa.PA_F32,
+                                ctypes.byref(f32), ctypes.c_void_p(0x3000), 4, ctypes.c_void_p(0x4000),
+                                ctypes.c_void_p(0x5000), 1, 16, 0.1, None)
+    assert r == pa.PA_ERR_UNSUPPORTED
+    r = pa.lib.pa_copy_blocks(ctypes.byref(p), None, 3, None)
+    assert r == pa.PA_ERR_INVALID
