@@ -2,14 +2,19 @@
 
 A step is one pass of the whole path over one batch: the host allocator
 appends the step's tokens (one per sequence for decode, the chunk for
-prefill) and packs block tables, slots and lengths into pinned buffers; they
-are copied to the device; copy-on-write copies run if any; the new K/V rows
-are written with pa_reshape_and_cache; then pa_decode (or pa_prefill_chunk)
-runs.  Inputs (pool contents, new rows, queries) are resident in HBM before
-the timed region.  The default workload is the LLaMA-13B-shaped decode
-batch.  One JSON line is printed.
+prefill) and packs block tables, slots and lengths into one pinned buffer,
+which is copied to the device once; then, for every attention layer the step
+serves, copy-on-write block copies (if any), pa_reshape_and_cache of the
+step's new K/V rows into that layer's pool, and pa_decode (or
+pa_prefill_chunk) over it.  The default workload is a decode step of an
+attention-only model with the LLaMA-13B shape (40 layers of 40 heads x 128,
+fp16 KV, 16-token blocks, 32 sequences of 128..2048 tokens); the block
+tables are shared by all layers, each layer has its own pool.  Pool contents,
+new rows and queries are resident in HBM before the timed region.  One JSON
+line is printed.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--layers N] [--partition-blocks P] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -37,37 +42,75 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-class Pinned:
-    """Two sets of pinned host buffers (alternating steps) and one device set."""
+class Timer:
+    """HIP events (torch.cuda.Event, timing enabled) recorded on the launch
+    stream immediately before and after one call."""
+
+    def __init__(self):
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.e0.record()
+
+    def stop(self):
+        self.e1.record()
+
+    def seconds(self):
+        return self.e0.elapsed_time(self.e1) * 1e-3
+
+
+class Staging:
+    """Per-step host->device inputs (slots, tables, lengths, copy pairs)
+    packed into one pinned buffer and sent with one copy on the compute
+    stream.  Two pinned buffers alternate steps so the host never rewrites
+    one that a queued copy has not read yet."""
 
     def __init__(self, shapes, device):
-        self.host = [{k: torch.empty(s, dtype=d, pin_memory=True) for k, (s, d) in shapes.items()}
-                     for _ in range(2)]
-        self.np = [{k: t.numpy() for k, t in h.items()} for h in self.host]
-        self.dev = {k: torch.empty(s, dtype=d, device=device) for k, (s, d) in shapes.items()}
-        self.done = [torch.cuda.Event(), torch.cuda.Event()]
-        for e in self.done:
+        self.layout, off = {}, 0
+        for k, (shape, dt) in shapes.items():
+            n = int(np.prod(shape)) * torch.empty((), dtype=dt).element_size()
+            self.layout[k] = (off, shape, dt, n)
+            off += (n + 255) // 256 * 256
+        self.host = [torch.empty(off, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        self.devb = torch.empty(off, dtype=torch.uint8, device=device)
+        self.np = [self._views(h, numpy=True) for h in self.host]
+        self.dev = self._views(self.devb)
+        self.copied = [torch.cuda.Event(), torch.cuda.Event()]
+        for e in self.copied:
             e.record()
+
+    def _views(self, buf, numpy=False):
+        out = {}
+        for k, (off, shape, dt, n) in self.layout.items():
+            v = buf[off:off + n].view(dt).view(shape)
+            out[k] = v.numpy() if numpy else v
+        return out
 
     def begin(self, k):
         b = k % 2
-        self.done[b].synchronize()     # copies out of this buffer (two steps ago) finished
+        self.copied[b].synchronize()     # the copy out of this pinned buffer has run
         return self.np[b]
 
     def upload(self, k):
         b = k % 2
-        for name, t in self.host[b].items():
-            self.dev[name].copy_(t, non_blocking=True)
-        self.done[b].record()
+        self.devb.copy_(self.host[b], non_blocking=True)
+        self.copied[b].record()
         return self.dev
+
 
 
 # ------------------------------------------------------------------ decode
 
 class DecodeBench:
-    """Decode steps over a batch: one new token per sequence per step."""
+    """Decode steps over a batch: one new token per sequence per step.
 
-    def __init__(self, workload, steps, warmup, device):
+    A step serves `layers` attention layers: one host allocation and one
+    upload of slots / tables / lengths (shared by every layer, as block tables
+    are), then, per layer, the cache write of the step's K/V into that
+    layer's pool and pa_decode over it."""
+
+    def __init__(self, workload, steps, warmup, device, partition_blocks=None, layers=None):
         self.name = workload
         cfg = W.CONFIGS[workload]
         self.cfg = cfg
@@ -81,37 +124,31 @@ class DecodeBench:
             lens0 = [int(x) for x in W.uniform_ints(cfg["seed"], self.B, cfg["len_lo"], cfg["len_hi"])]
             self.N = cfg["num_blocks"]
             self.pb = 0
+            self.layers = 40 if layers is None else layers   # LLaMA-13B has 40 layers
         elif workload == "prefix_cow":
             self.B = cfg["batch"]
             suffix = W.uniform_ints(cfg["seed"], self.B, cfg["suffix_lo"], cfg["suffix_hi"])
             lens0 = [cfg["prefix"] + int(s) + 1 for s in suffix]
             self.N = cfg["num_blocks"]
             self.pb = 0
+            self.layers = 1 if layers is None else layers
         elif workload == "long_fp8_decode":
             self.B = cfg["batch"]
             lens0 = [cfg["context"]] * self.B
             # room for the timed steps' growth beyond the 16384 blocks of the context
             self.N = cfg["num_blocks"] + self.B * (-(-total // self.bs) + 1)
             self.pb = cfg["partition_blocks"]
+            self.layers = 1 if layers is None else layers
         else:
             raise ValueError(workload)
+        if partition_blocks is not None:
+            self.pb = partition_blocks
         self.lens0 = lens0
         self.alloc = pa.Allocator(self.N, self.bs, W.free_order(cfg["seed"], self.N))
-        self.pool = pa.PagedPool.empty(self.N, self.H, self.bs, self.D, self.kv, device)
         g = torch.Generator(device=device)
         g.manual_seed(cfg["seed"])
-        for t in (self.pool.k_cache, self.pool.v_cache):
-            if self.kv == "fp8":
-                # codes of N(0,1)/scale values: draw normal values, take the codes
-                for i in range(0, self.N, 1024):
-                    x = torch.randn((min(1024, self.N - i),) + tuple(t.shape[1:]), generator=g,
-                                    device=device) * 40.0
-                    t[i:i + x.shape[0]] = x.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
-            else:
-                t.copy_(torch.randn(t.shape, generator=g, device=device).to(t.dtype))
-        if self.kv == "fp8":
-            self.pool.k_scale.fill_(1.0 / 40.0)
-            self.pool.v_scale.fill_(1.0 / 40.0)
+        self.pools = [self._filled_pool(g) for _ in range(self.layers)]
+        self.pool = self.pools[0]
         # sequences: the prompt holds every token but the step's own
         if workload == "prefix_cow":
             self.alloc.alloc_prompt(0, cfg["prefix"])
@@ -124,10 +161,10 @@ class DecodeBench:
                 self.alloc.alloc_prompt(i, lens0[i] - 1)
         self.ids = np.arange(self.B, dtype=np.int64)
         self.maxb = -(-(max(lens0) + total) // self.bs)
-        self.bufs = Pinned({"slots": ((self.B, 1), torch.int64),
-                            "tables": ((self.B, self.maxb), torch.int32),
-                            "lens": ((self.B,), torch.int32),
-                            "cow": ((self.B, 2), torch.int32)}, device)
+        self.bufs = Staging({"slots": ((self.B, 1), torch.int64),
+                             "tables": ((self.B, self.maxb), torch.int32),
+                             "lens": ((self.B,), torch.int32),
+                             "cow": ((self.B, 2), torch.int32)}, device)
         tdt = pa.TORCH_DTYPE
         in_dt = tdt["bf16"] if self.kv == "fp8" else tdt[self.kv]
         self.knew = [torch.randn((self.B, self.H, self.D), generator=g, device=device).to(in_dt)
@@ -143,6 +180,22 @@ class DecodeBench:
         self.step_bytes = []
         self.cows = 0
 
+    def _filled_pool(self, g):
+        pool = pa.PagedPool.empty(self.N, self.H, self.bs, self.D, self.kv, self.device)
+        for t in (pool.k_cache, pool.v_cache):
+            for i in range(0, self.N, 1024):
+                n = min(1024, self.N - i)
+                x = torch.randn((n,) + tuple(t.shape[1:]), generator=g, device=self.device)
+                if self.kv == "fp8":
+                    # codes of values drawn N(0, 40^2) with scale 1/40: N(0,1) after scaling
+                    t[i:i + n] = (x * 40.0).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+                else:
+                    t[i:i + n] = x.to(t.dtype)
+        if self.kv == "fp8":
+            pool.k_scale.fill_(1.0 / 40.0)
+            pool.v_scale.fill_(1.0 / 40.0)
+        return pool
+
     def step(self, k, timed):
         h = self.bufs.begin(k)
         _, _, ncow = self.alloc.append_tokens_batch(self.ids, 1, slots_out=h["slots"],
@@ -150,19 +203,28 @@ class DecodeBench:
         self.alloc.pack(self.ids, self.maxb, tables_out=h["tables"], lens_out=h["lens"])
         lens = h["lens"].copy()
         d = self.bufs.upload(k)
+        pairs = None
         if ncow:
-            pairs = d["cow"][torch.from_numpy(h["cow"][:, 0] >= 0).to(self.device)]
-            pa.pa_copy_blocks(self.pool, pairs.contiguous())
+            pairs = d["cow"][torch.from_numpy(h["cow"][:, 0] >= 0).to(self.device)].contiguous()
             self.cows += ncow
-        pa.pa_reshape_and_cache(self.pool, self.knew[k % 4], self.vnew[k % 4], d["slots"].view(-1))
+        for li, pool in enumerate(self.pools):
+            if pairs is not None:
+                pa.pa_copy_blocks(pool, pairs)
+            pa.pa_reshape_and_cache(pool, self.knew[(k + li) % 4], self.vnew[(k + li) % 4],
+                                    d["slots"].view(-1))
+            # one launch per step (layer 0) carries the event pair: an event
+            # record waits for the caches to be written back, which would
+            # otherwise stall every layer
+            timing = timed and li == 0
+            if timing:
+                tm = Timer()
+                tm.start()
+            pa.pa_decode(self.out, self.q[(k + li) % 4], pool, d["tables"], d["lens"], self.scale,
+                         self.pb, self.ws)
+            if timing:
+                tm.stop()
+                self.ev.append(tm)
         if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        pa.pa_decode(self.out, self.q[k % 4], self.pool, d["tables"], d["lens"], self.scale, self.pb,
-                     self.ws)
-        if timed:
-            e1.record()
-            self.ev.append((e0, e1))
             self.step_bytes.append(self.decode_bytes(lens))
 
     def decode_bytes(self, lens):
@@ -178,14 +240,14 @@ class DecodeBench:
         return kv + qo + tables + scales
 
     def kernel_stats(self):
-        times = [a.elapsed_time(b) * 1e-3 for a, b in self.ev]
-        t = float(np.mean(times))
-        bytes_ = float(np.mean(self.step_bytes))
-        return t, bytes_
+        """Mean pa_decode launch time (s) and mean algorithmic bytes per launch."""
+        times = [t.seconds() for t in self.ev]
+        return float(np.mean(times)), float(np.mean(self.step_bytes))
 
     def workload_config(self):
         c = self.cfg
-        d = {"workload": self.name, "batch": self.B, "num_heads": self.H, "head_dim": self.D,
+        d = {"workload": self.name, "layers_per_step": self.layers, "batch": self.B,
+             "num_heads": self.H, "head_dim": self.D,
              "block_size": self.bs, "kv_dtype": self.kv, "q_dtype": self.qdt,
              "pool_blocks": self.N, "mean_context": float(np.mean(self.lens0))}
         if self.name == "llama13b_decode":
@@ -253,9 +315,9 @@ class PrefillBench:
         self.q = torch.randn((T, self.H, self.D), generator=g, device=device).to(torch.bfloat16)
         self.out = torch.empty((T, self.H, self.D), dtype=torch.bfloat16, device=device)
         self.maxb = -(-(max(self.ctx) + self.S) // self.bs)
-        self.bufs = Pinned({"slots": ((self.B, self.S), torch.int64),
-                            "tables": ((self.B, self.maxb), torch.int32),
-                            "lens": ((self.B,), torch.int32)}, device)
+        self.bufs = Staging({"slots": ((self.B, self.S), torch.int64),
+                             "tables": ((self.B, self.maxb), torch.int32),
+                             "lens": ((self.B,), torch.int32)}, device)
         self.qsl = torch.tensor(np.arange(self.B + 1) * self.S, dtype=torch.int32, device=device)
         self.scale = 1 / math.sqrt(self.D)
         self.ev, self.next_id = [], 0
@@ -271,13 +333,13 @@ class PrefillBench:
         d = self.bufs.upload(k)
         pa.pa_reshape_and_cache(self.pool, self.knew, self.vnew, d["slots"].view(-1))
         if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            tm = Timer()
+            tm.start()
         pa.pa_prefill_chunk(self.out, self.q, self.pool, d["tables"], d["lens"], self.qsl, self.S,
                             self.scale)
         if timed:
-            e1.record()
-            self.ev.append((e0, e1))
+            tm.stop()
+            self.ev.append(tm)
         for s in ids:
             self.alloc.free_seq(int(s))
 
@@ -287,7 +349,7 @@ class PrefillBench:
         return 4.0 * self.D * self.H * pairs
 
     def kernel_stats(self):
-        t = float(np.mean([a.elapsed_time(b) * 1e-3 for a, b in self.ev]))
+        t = float(np.mean([tm.seconds() for tm in self.ev]))
         return t, self.flops()
 
     def workload_config(self):
@@ -344,6 +406,11 @@ def main():
     ap.add_argument("--workload", default="llama13b_decode",
                     choices=["llama13b_decode", "prefix_cow", "chunked_prefill", "long_fp8_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="attention layers per decode step (default: 40 for the LLaMA-13B shape)")
+    ap.add_argument("--partition-blocks", type=int, default=None,
+                    help="decode split-K partition size in blocks (default: the library's choice, "
+                         "or the workload's own)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -356,7 +423,8 @@ def main():
     if args.workload == "chunked_prefill":
         b = PrefillBench(args.steps, args.warmup, device)
     else:
-        b = DecodeBench(args.workload, args.steps, args.warmup, device)
+        b = DecodeBench(args.workload, args.steps, args.warmup, device, args.partition_blocks,
+                        args.layers)
     torch.cuda.synchronize()
     for k in range(args.warmup):
         b.step(k, False)
@@ -381,17 +449,19 @@ def main():
                            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
                            "kernel": "prefill_kernel", "kernel_us": kt * 1e6}
     else:
-        kv_bytes = work
+        kv_bytes = work                   # per launch (one layer)
+        step_s = wall / args.steps
         res.update(metric=METRIC if args.workload == "llama13b_decode"
                    else f"pa_decode KV GB/s at the {args.workload} workload",
-                   value=kv_bytes / (wall / args.steps) / 1e9, unit="GB/s", dtype=b.kv)
+                   value=kv_bytes * b.layers / step_s / 1e9, unit="GB/s", dtype=b.kv)
         ach = kv_bytes / kt / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "decode_kernel",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                           "kernel": "pa_decode (decode_kernel + decode_merge_kernel)",
                            "kernel_us": kt * 1e6, "bytes_per_launch": kv_bytes}
-        res["decode_tokens_per_s"] = b.B / (wall / args.steps)
-        res["decode_tokens_per_s_40_layers"] = b.B / (40 * wall / args.steps)
-        res["pa_decode_tokens_per_s"] = b.B / kt
+        res["hbm_frac_step"] = kv_bytes * b.layers / step_s / 1e9 / HBM_PEAK_GBS
+        res["decode_tokens_per_s"] = b.B / step_s
+        res["pa_decode_us_per_layer"] = kt * 1e6
     if not args.no_cpu_baseline:
         log("bench: cpu baseline")
         res["cpu_baseline"] = b.cpu_baseline()

@@ -110,18 +110,12 @@ int32_t pa_decode_auto_partition_blocks(const pa_pool* pool, int32_t num_seqs,
 
 /*
  * Bytes of device workspace pa_decode needs for these arguments (0 when every
- * sequence fits in one partition).  The workspace holds per-partition partial
- * results and one counter per (sequence, head).
+ * sequence fits in one partition): the (max, sum) pair and the unnormalised
+ * output of every (sequence, head, partition), float32.  No initialisation is
+ * needed.
  */
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
                                  int32_t max_blocks_per_seq, int32_t partition_blocks);
-
-/*
- * pa_decode_workspace_init -- zero the counters of a fresh workspace (a small
- * kernel on the stream; no memset node).  Every complete pa_decode call leaves
- * them zero again, so this is needed once after allocating the workspace.
- */
-pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pa_decode -- attention of one query token per sequence over its paged K/V
@@ -137,13 +131,12 @@ pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, hipS
  *   block_tables  device, [num_seqs][max_blocks_per_seq] int32; only the first
  *                 ceil(L / block_size) entries of a row are read.
  *   context_lens  device, [num_seqs] int32, 0 <= L <= max_blocks_per_seq*block_size.
- *   partition_blocks  blocks per split-K partition (0 = automatic).  Sequences
- *                 longer than one partition are split; the partials are merged
- *                 with a running-max / running-sum reduction inside the same
- *                 kernel (the last partition of a (sequence, head) to finish
- *                 does the merge).
- *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, counters
- *                 zeroed once by pa_decode_workspace_init.  Calls that share a
+ *   partition_blocks  blocks per split-K partition, 1..256 (0 = automatic).
+ *                 Sequences longer than one partition are split; the
+ *                 partitions' (max, sum, output) triples are merged by a
+ *                 second, small kernel on the same stream.
+ *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 256-byte
+ *                 aligned (may be NULL when that is 0).  Calls that share a
  *                 workspace must be ordered (same stream).
  */
 pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,

@@ -35,7 +35,7 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
 # Every symbol the header declares; checked at load time.
 EXPORTS = [
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_auto_partition_blocks",
-    "pa_decode_workspace_bytes", "pa_decode_workspace_init", "pa_decode", "pa_prefill_chunk",
+    "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_chunk",
     "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_prompt", "pa_append_tokens",
     "pa_append_tokens_batch", "pa_fork", "pa_free_seq", "pa_get_block_table",
     "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
@@ -67,7 +67,6 @@ def _load():
         "pa_copy_blocks": (I32, [P, VP, I32, VP]),
         "pa_decode_auto_partition_blocks": (I32, [P, I32, I32]),
         "pa_decode_workspace_bytes": (SZ, [P, I32, I32, I32]),
-        "pa_decode_workspace_init": (I32, [VP, SZ, VP]),
         "pa_decode": (I32, [VP, I32, VP, I32, P, VP, I32, VP, I32, ctypes.c_float, I32, VP, SZ, VP]),
         "pa_prefill_chunk": (I32, [VP, I32, VP, I32, P, VP, I32, VP, VP, I32, I32, ctypes.c_float,
                                    VP]),
@@ -202,15 +201,12 @@ def pa_decode_workspace_bytes(pool, num_seqs, max_blocks_per_seq, partition_bloc
     return lib.pa_decode_workspace_bytes(pool.ref(), num_seqs, max_blocks_per_seq, partition_blocks)
 
 
-def decode_workspace(pool, num_seqs, max_blocks_per_seq, partition_blocks=0, stream=None):
-    """A zero-initialised workspace tensor for pa_decode (or None if unneeded)."""
+def decode_workspace(pool, num_seqs, max_blocks_per_seq, partition_blocks=0):
+    """A workspace tensor for pa_decode (or None if none is needed)."""
     n = pa_decode_workspace_bytes(pool, num_seqs, max_blocks_per_seq, partition_blocks)
     if n == 0:
         return None
-    ws = torch.empty(n, dtype=torch.uint8, device=pool.device)
-    _check(lib.pa_decode_workspace_init(_ptr(ws), n, _stream(stream, pool.device)),
-           "pa_decode_workspace_init")
-    return ws
+    return torch.empty(n, dtype=torch.uint8, device=pool.device)
 
 
 def pa_decode(out, q, pool, block_tables, context_lens, scale, partition_blocks=0,

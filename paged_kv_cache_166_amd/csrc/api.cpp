@@ -40,13 +40,16 @@ pa_status hip_status(const char* fn, hipError_t e) {
   return PA_OK;
 }
 
+// 512 tokens per partition: long enough that a workgroup's fixed costs
+// (table and query loads, the final merge) are small next to its stream of
+// K/V, short enough that ragged batches still split into many workgroups.
 int32_t auto_partition_blocks(const pa_pool* p) {
-  int32_t b = 256 / p->block_size;
-  return b < 1 ? 1 : (b > 64 ? 64 : b);
+  int32_t b = 512 / p->block_size;
+  return b < 1 ? 1 : (b > 256 ? 256 : b);
 }
 
 struct WsLayout {
-  int64_t cnt_off, ml_off, acc_off, bytes;
+  int64_t ml_off, acc_off, bytes;
   int32_t parts;
 };
 
@@ -56,9 +59,8 @@ WsLayout ws_layout(const pa_pool* p, int32_t num_seqs, int32_t max_blocks, int32
   if (w.parts <= 1) return w;
   const int64_t sh = int64_t(num_seqs) * p->num_heads;
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  w.cnt_off = 0;
-  w.ml_off = up(sh * 4);
-  w.acc_off = w.ml_off + up(sh * w.parts * 2 * 4);
+  w.ml_off = 0;
+  w.acc_off = up(sh * w.parts * 2 * 4);
   w.bytes = w.acc_off + up(sh * w.parts * p->head_dim * 4);
   return w;
 }
@@ -126,15 +128,6 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
   return size_t(ws_layout(pool, num_seqs, max_blocks_per_seq, pb).bytes);
 }
 
-pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (workspace_bytes == 0) return PA_OK;
-  if (!workspace || !aligned(workspace, 256))
-    return fail(PA_ERR_INVALID, "pa_decode_workspace_init: workspace must be 256-byte aligned");
-  return hip_status("pa_decode_workspace_init",
-                    pa::launch_zero_i32(static_cast<int32_t*>(workspace),
-                                        int64_t(workspace_bytes / 4), stream));
-}
-
 pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
                     const pa_pool* pool, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
@@ -157,8 +150,8 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
   }
   if (out_dtype != PA_F32 && out_dtype != q_dtype)
     return fail(PA_ERR_INVALID, "%s: out_dtype must be f32 or q_dtype", fn);
-  if (partition_blocks < 0 || partition_blocks > 64)
-    return fail(PA_ERR_UNSUPPORTED, "%s: partition_blocks %d (1..64, or 0 = auto)", fn,
+  if (partition_blocks < 0 || partition_blocks > 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: partition_blocks %d (1..256, or 0 = auto)", fn,
                 partition_blocks);
   const int32_t pb = partition_blocks > 0 ? partition_blocks : auto_partition_blocks(pool);
   const WsLayout w = ws_layout(pool, num_seqs, max_blocks_per_seq, pb);
@@ -177,11 +170,11 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
   a.v_scale = pool->v_scale;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.ws_cnt = w.parts > 1 ? reinterpret_cast<int32_t*>(ws + w.cnt_off) : nullptr;
   a.ws_ml = w.parts > 1 ? reinterpret_cast<float*>(ws + w.ml_off) : nullptr;
   a.ws_acc = w.parts > 1 ? reinterpret_cast<float*>(ws + w.acc_off) : nullptr;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_heads = pool->num_heads;
+  a.block_size = pool->block_size;
   a.part_blocks = pb;
   a.max_parts = w.parts < 1 ? 1 : w.parts;
   a.scale_log2 = scale * 1.4426950408889634f;

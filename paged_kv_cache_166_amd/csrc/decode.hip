@@ -7,12 +7,12 @@
 //
 // How (decode is a gather-GEMV: ~1 flop per byte, so HBM bandwidth bounds it
 // and MFMA has nothing to do here):
-//  * grid (partition, head, sequence); a workgroup of NW wavefronts owns one
-//    partition of `part_blocks` blocks of one (sequence, head); wave w takes
-//    blocks w, w+NW, ... of the partition;
-//  * the partition's block-table entries are read once into a VGPR (lane t
-//    holds entry t) and each block id is moved to an SGPR with readlane, so
-//    every tile address is scalar;
+//  * grid (head, sequence, partition); a workgroup of NW wavefronts owns one
+//    partition of `part_blocks` blocks (up to 256) of one (sequence, head);
+//    wave w takes blocks w, w+NW, ... of the partition;
+//  * a wave's block-table entries are read once into one VGPR (lane t holds
+//    the id of the wave's t-th block) and each id is moved to an SGPR with
+//    readlane, so every tile address is uniform;
 //  * one (block, head) tile is contiguous in the [N][H][bs][D] pool; a
 //    wave-wide 16-byte-per-lane load covers 1 KiB of it, so K and V tiles are
 //    read with fully coalesced dwordx4 loads straight into registers (each
@@ -24,11 +24,17 @@
 //    sum (online softmax) over the rows it sees -- no cross-group traffic in
 //    the loop;
 //  * the next block's K and V loads are issued before the current block is
-//    consumed (two register buffers);
+//    consumed (two register buffers), unconditionally: past the wave's last
+//    block they re-read that block (an L2 hit), so the number of loads in
+//    flight is the same on every path and the compiler's waits keep exactly
+//    one block outstanding while the current one is consumed;
 //  * at the end the groups, then the waves, merge their (max, sum, acc)
-//    triples; a partition writes its triple to the workspace and the last
-//    partition of a (sequence, head) to finish (an atomic counter) merges all
-//    of them and writes the output, so split-K needs no second kernel.
+//    triples; a sequence that fits one partition writes its output directly,
+//    otherwise each partition writes its triple to the workspace and a small
+//    second kernel merges the triples of each (sequence, head).  (Merging in
+//    the last partition to finish would need device-scope release/acquire
+//    fences per workgroup; on this chip they write back and invalidate the
+//    whole L2 and cost far more than a second launch.)
 // Scores live in the log2 domain: s = log2(e) * scale * q.k, p = exp2(s - m).
 #include "device.h"
 #include "kernels.h"
@@ -168,6 +174,8 @@ struct KvOps<PA_FP8_E4M3> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr int kMaxPartBlocks = 256;
+
 template <int KV, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using G = Geo<KV, D, BS>;
@@ -175,9 +183,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   constexpr int E = G::kEpl;
   static_assert(E == Ops::kEpl, "lane element count");
 
-  const int part = blockIdx.x;
-  const int head = blockIdx.y;
-  const int seq = blockIdx.z;
+  // Heads of one (sequence, partition) are adjacent in the dispatch order
+  // (they read the same blocks, one tile apart); the highest partitions,
+  // which only the longest sequences have, are dispatched first.
+  const int head = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int part = a.max_parts - 1 - int(blockIdx.z);
   const int H = a.num_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -200,9 +211,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int col = lane % G::kLpr;
   const bool row_ok = !G::kIdleGroups || grp < BS;
 
-  // Block ids of this partition: lane t holds entry blk0 + t.
+  // This wave's blocks are wave, wave + NW, ... of the partition (n_w <= 64
+  // of them); lane t holds the block id of the wave's t-th block.
+  const int n_w = wave < nb ? (nb - wave + NW - 1) / NW : 0;
   const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq + blk0;
-  const int tab = lane < nb ? table[lane] : 0;
+  const int tab = lane < n_w ? table[wave + NW * lane] : 0;
+  static_assert(kMaxPartBlocks <= 64 * NW, "one table register per wave");
 
   const typename Ops::Q q = Ops::load_q(a.q, out_off + col * E, a.q_dtype);
   const int64_t blk_stride = int64_t(H) * G::kTileBytes;
@@ -217,8 +231,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   uint4 k0[G::kLoads], v0[G::kLoads], k1[G::kLoads], v1[G::kLoads];
   int p0 = 0, p1 = 0;
 
-  auto issue = [&](uint4* kr, uint4* vr, int& phys, int jl) {
-    phys = __builtin_amdgcn_readlane(tab, jl);
+  auto issue = [&](uint4* kr, uint4* vr, int& phys, int i) {
+    phys = __builtin_amdgcn_readlane(tab, i);
     const char* kp = kbase + int64_t(phys) * blk_stride;
     const char* vp = vbase + int64_t(phys) * blk_stride;
 #pragma unroll
@@ -276,19 +290,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     m = mx;
   };
 
-  // Two-deep software pipeline over this wave's blocks wave, wave+NW, ...
-  int jl = wave;
-  if (jl < nb) issue(k0, v0, p0, jl);
-  while (jl < nb) {
-    int jn = jl + NW;
-    if (jn < nb) issue(k1, v1, p1, jn);
-    consume(k0, v0, p0, jl);
-    jl = jn;
-    if (jl >= nb) break;
-    jn = jl + NW;
-    if (jn < nb) issue(k0, v0, p0, jn);
-    consume(k1, v1, p1, jl);
-    jl = jn;
+  // Two-deep software pipeline over this wave's n_w blocks; the prefetch
+  // past the last one re-reads the last one.
+  if (n_w > 0) {
+    issue(k0, v0, p0, 0);
+    for (int i = 0;;) {
+      issue(k1, v1, p1, min(i + 1, n_w - 1));
+      consume(k0, v0, p0, wave + i * NW);
+      if (++i >= n_w) break;
+      issue(k0, v0, p0, min(i + 1, n_w - 1));
+      consume(k1, v1, p1, wave + i * NW);
+      if (++i >= n_w) break;
+    }
   }
 
   // Merge the groups of this wave (lanes with equal col, different grp).
@@ -308,7 +321,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // Merge the waves through LDS.
   __shared__ float sm_acc[NW][D];
   __shared__ float sm_m[NW], sm_l[NW];
-  __shared__ int s_last;
   if (lane < G::kLpr) {
 #pragma unroll
     for (int e = 0; e < E; ++e) sm_acc[wave][col * E + e] = acc[e];
@@ -336,48 +348,53 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     return;
   }
 
-  // Split-K: publish this partition's triple, the last one merges.
-  const int64_t sh = int64_t(seq) * H + head;
-  const int64_t pidx = sh * a.max_parts + part;
+  // Split-K: publish this partition's (max, sum, acc) for the merge kernel.
+  const int64_t pidx = (int64_t(seq) * H + head) * a.max_parts + part;
   if (tid < D) a.ws_acc[pidx * D + tid] = A;
   if (tid == 0) {
     a.ws_ml[2 * pidx] = M;
     a.ws_ml[2 * pidx + 1] = S;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.ws_cnt[sh], 1) == nparts - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid < D) {
-    const float* ml = a.ws_ml + 2 * sh * a.max_parts;
-    const float* pa = a.ws_acc + sh * a.max_parts * D + tid;
-    float Mg = kNoMax;
-    for (int p = 0; p < nparts; ++p) Mg = fmaxf(Mg, ml[2 * p]);
-    float Ag = 0.f, Sg = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-      const float f = fast_exp2(ml[2 * p] - Mg);
-      Sg = fmaf(ml[2 * p + 1], f, Sg);
-      Ag = fmaf(pa[int64_t(p) * D], f, Ag);
-    }
-    store_from_f32(a.out, out_off + tid, a.out_dtype, Sg > 0.f ? Ag / Sg : 0.f);
-  }
-  if (tid == 0) atomicExch(&a.ws_cnt[sh], 0);
 }
 
-__global__ void zero_i32_kernel(int32_t* p, int64_t n) {
-  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
-       i += int64_t(gridDim.x) * blockDim.x)
-    p[i] = 0;
+// Merge the partitions of each (sequence, head) that has more than one:
+// M = max_p m_p, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  const int head = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int H = a.num_heads;
+  const int d = threadIdx.x;
+  const int L = a.context_lens[seq];
+  const int nblocks = (L + a.block_size - 1) / a.block_size;
+  const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
+  if (nparts <= 1) return;
+  const int64_t sh = int64_t(seq) * H + head;
+  const float* ml = a.ws_ml + 2 * sh * a.max_parts;
+  const float* pa = a.ws_acc + sh * a.max_parts * D + d;
+  // One pass with a running maximum, so all loads can be in flight together.
+  float M = kNoMax, A = 0.f, S = 0.f;
+#pragma unroll 8
+  for (int p = 0; p < nparts; ++p) {
+    const float m = ml[2 * p], l = ml[2 * p + 1], x = pa[int64_t(p) * D];
+    const float Mn = fmaxf(M, m);
+    const float fo = fast_exp2(M - Mn), fn = fast_exp2(m - Mn);
+    S = S * fo + l * fn;
+    A = A * fo + x * fn;
+    M = Mn;
+  }
+  store_from_f32(a.out, sh * D + d, a.out_dtype, S > 0.f ? A / S : 0.f);
 }
 
 constexpr int kWaves = 4;
 
 template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
-  dim3 grid(a.max_parts, a.num_heads, num_seqs);
+  dim3 grid(a.num_heads, num_seqs, a.max_parts);
   hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, a);
+  if (a.max_parts > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_heads, num_seqs), dim3(D), 0, stream,
+                       a);
   return hipGetLastError();
 }
 
@@ -410,14 +427,6 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int bl
     case PA_FP8_E4M3: return launch_d<PA_FP8_E4M3>(a, head_dim, block_size, num_seqs, stream);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  int blocks = int((n + 255) / 256);
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(256), 0, stream, p, n);
-  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -18,9 +18,9 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* ws_acc;    // [num_seqs][num_heads][max_parts][head_dim]
   float* ws_ml;     // [num_seqs][num_heads][max_parts][2]  (max, sum)
-  int32_t* ws_cnt;  // [num_seqs][num_heads]
   int32_t max_blocks_per_seq;
   int32_t num_heads;
+  int32_t block_size;
   int32_t part_blocks;
   int32_t max_parts;
   float scale_log2;  // scale * log2(e)
@@ -30,7 +30,6 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
                          int num_seqs, hipStream_t stream);
-hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
 
 struct CacheWriteArgs {
   void* k_cache;

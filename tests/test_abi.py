@@ -61,7 +61,7 @@ def test_decode_argument_checks_before_launch():
     assert _decode(p, q_dtype=pa.PA_BF16) == pa.PA_ERR_UNSUPPORTED     # q must match f16 pool
     assert _decode(p, out_dtype=pa.PA_BF16) == pa.PA_ERR_INVALID       # out f32 or q dtype
     assert _decode(p, q=0x40004) == pa.PA_ERR_INVALID                  # q alignment
-    assert _decode(p, pb=65) == pa.PA_ERR_UNSUPPORTED
+    assert _decode(p, pb=257) == pa.PA_ERR_UNSUPPORTED
     assert _decode(p, B=0) == pa.PA_OK                                 # nothing to do
     # 128 blocks at 16 per partition -> 8 partitions: a workspace is required
     assert _decode(p, maxb=128, pb=16) == pa.PA_ERR_INVALID
@@ -76,9 +76,9 @@ def test_workspace_sizes():
     p = _fake_pool()
     assert pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 4, 16, 16) == 0   # one partition
     b = pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 4, 33, 16)          # three partitions
-    # counters, (max, sum) and acc per (seq, head, partition), each 256-byte padded
-    assert b == 256 + 256 + ((4 * 2 * 3 * 128 * 4 + 255) // 256) * 256
-    assert pa.lib.pa_decode_auto_partition_blocks(ctypes.byref(p), 4, 33) == 16
+    # (max, sum) and acc per (seq, head, partition), each 256-byte padded
+    assert b == 256 + ((4 * 2 * 3 * 128 * 4 + 255) // 256) * 256
+    assert pa.lib.pa_decode_auto_partition_blocks(ctypes.byref(p), 4, 33) == 32   # 512 tokens
 
 
 def test_reshape_and_prefill_checks():

@@ -80,7 +80,7 @@ def test_decode_sweep(kv, D, bs):
     q_dev, q64 = sc.random_q(len(seqs), qdt)
     scale = 1 / math.sqrt(D)
     ref = _oracle(sc, seqs, q64, scale)
-    for pb in (0, 1, 3, 64):
+    for pb in (0, 1, 3, 64, 77, 256):
         got, _, _ = _run_decode(sc, seqs, q_dev, scale, pb)
         assert_close(got, ref, TOL[kv], f"{kv} D={D} bs={bs} pb={pb}")
         assert np.all(got[0] == 0.0)                      # empty sequence -> zeros
@@ -121,7 +121,7 @@ def test_llama13b_decode_workload():
     q_dev, q64 = sc.random_q(cfg["batch"], "f16")
     scale = 1 / math.sqrt(cfg["head_dim"])
     ref = _oracle(sc, seqs, q64, scale)
-    for pb in (0, 8, 64):
+    for pb in (0, 8, 64, 128):
         got, _, _ = _run_decode(sc, seqs, q_dev, scale, pb, max_blocks=2048 // 16)
         err = assert_close(got, ref, TOL["f16"], f"llama13b pb={pb}")
         print(f"llama13b pb={pb}: max abs err {err:.2e}, rel {err / np.abs(ref).max():.2e}")
