@@ -359,12 +359,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
 // Merge the partitions of each (sequence, head) that has more than one:
 // M = max_p m_p, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
-template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+// R threads per output element take every R-th partition with a running
+// maximum (all their loads can be in flight together), then combine in LDS.
+template <int D, int R>
+__global__ __launch_bounds__(D * R) void decode_merge_kernel(DecodeArgs a) {
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
   const int H = a.num_heads;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x % D;
+  const int r = threadIdx.x / D;
   const int L = a.context_lens[seq];
   const int nblocks = (L + a.block_size - 1) / a.block_size;
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
@@ -372,10 +375,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int64_t sh = int64_t(seq) * H + head;
   const float* ml = a.ws_ml + 2 * sh * a.max_parts;
   const float* pa = a.ws_acc + sh * a.max_parts * D + d;
-  // One pass with a running maximum, so all loads can be in flight together.
   float M = kNoMax, A = 0.f, S = 0.f;
-#pragma unroll 8
-  for (int p = 0; p < nparts; ++p) {
+#pragma unroll 4
+  for (int p = r; p < nparts; p += R) {
     const float m = ml[2 * p], l = ml[2 * p + 1], x = pa[int64_t(p) * D];
     const float Mn = fmaxf(M, m);
     const float fo = fast_exp2(M - Mn), fn = fast_exp2(m - Mn);
@@ -383,7 +385,23 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
     A = A * fo + x * fn;
     M = Mn;
   }
-  store_from_f32(a.out, sh * D + d, a.out_dtype, S > 0.f ? A / S : 0.f);
+  __shared__ float sm_a[R][D], sm_m[R][D], sm_s[R][D];
+  sm_a[r][d] = A;
+  sm_m[r][d] = M;
+  sm_s[r][d] = S;
+  __syncthreads();
+  if (r != 0) return;
+  float Mg = kNoMax;
+#pragma unroll
+  for (int i = 0; i < R; ++i) Mg = fmaxf(Mg, sm_m[i][d]);
+  float Ag = 0.f, Sg = 0.f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const float f = fast_exp2(sm_m[i][d] - Mg);
+    Ag = fmaf(sm_a[i][d], f, Ag);
+    Sg = fmaf(sm_s[i][d], f, Sg);
+  }
+  store_from_f32(a.out, sh * D + d, a.out_dtype, Sg > 0.f ? Ag / Sg : 0.f);
 }
 
 constexpr int kWaves = 4;
@@ -392,9 +410,10 @@ template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
   dim3 grid(a.num_heads, num_seqs, a.max_parts);
   hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, a);
+  constexpr int R = 512 / D;
   if (a.max_parts > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_heads, num_seqs), dim3(D), 0, stream,
-                       a);
+    hipLaunchKernelGGL((decode_merge_kernel<D, R>), dim3(a.num_heads, num_seqs), dim3(D * R), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
