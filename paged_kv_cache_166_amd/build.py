@@ -24,8 +24,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-I/opt/rocm/include", "-Wall",
           "-Wno-unused-function"]
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs (gfx950 allows
+# it); otherwise the compiler parks them in AGPRs and copies them back and
+# forth around every softmax step of the prefill kernel.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+          "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src):

@@ -18,7 +18,8 @@
 //  * the accumulator layout of S^T gives every lane one query column and 16
 //    of the tile's keys, so the online softmax (running max m, running sum
 //    l, exp2 of log2-scaled scores) is lane-local plus one exchange between
-//    the two half-waves;
+//    the two half-waves; a row's reference maximum (and so the accumulator
+//    rescale) moves only when the row maximum grows by more than 2^8;
 //  * O^T += V^T P^T on v_mfma_f32_32x32x16_f16: P (rounded to fp16) is used
 //    straight from the S^T accumulators as the B operand -- the contraction
 //    index is permuted to match the accumulator layout and V^T is read from
@@ -28,6 +29,8 @@
 // Workgroups are mapped so that all query tiles of one (sequence, head) run
 // on the same XCD (its L2 holds that head's K/V); the last query tile, which
 // sees the most keys, is dispatched first.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -45,6 +48,7 @@ constexpr int kBM = kWaves * kQW;       // query rows per workgroup
 constexpr int kBN = 32;                 // keys per tile
 constexpr int kVtStride = 72;           // bytes per dimension row of V^T in LDS
 constexpr int kXcds = 8;
+constexpr int kPrefetch = 2;            // K/V tiles in flight ahead of the one consumed
 
 template <int KV>
 __device__ __forceinline__ f32x16_t mfma_qk(uint4 a, uint4 b, f32x16_t c) {
@@ -61,34 +65,96 @@ __device__ __forceinline__ f32x16_t mfma_pv(uint4 a, uint4 b, f32x16_t c) {
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed fp16 pair, RNE (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+
 // Two 16-bit values of the pool's type -> packed fp16 pair (RNE).
 template <int KV>
 __device__ __forceinline__ uint32_t to_f16x2(uint32_t w) {
   if constexpr (KV == PA_F16) return w;
-  const uint32_t lo = f32_to_f16_bits(bf16_lo(w));
-  const uint32_t hi = f32_to_f16_bits(bf16_hi(w));
-  return lo | (hi << 16);
+  return pack_f16(bf16_lo(w), bf16_hi(w));
 }
 
-__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  return uint32_t(f32_to_f16_bits(a)) | (uint32_t(f32_to_f16_bits(b)) << 16);
+// Low / high 16-bit halves of x and y side by side: (x.lo, y.lo), (x.hi, y.hi).
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+
+// The running maximum a query row's weights are taken against moves only
+// when the row's maximum grows by more than this (log2 units): weights stay
+// below 2^8, well inside fp16, and the accumulator is rescaled rarely.
+constexpr float kRescaleSlack = 8.0f;
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding, the
+// other counters unconstrained (vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14).
+constexpr int wait_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
+// s_waitcnt immediate: all LDS / scalar-memory operations done.
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+
+typedef __attribute__((address_space(3))) void lds_t;
+
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane i's bytes land at dst + 16 i; dst is
+// wave-uniform.
+__device__ __forceinline__ void load_lds16(const void* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_t*)dst, 16, 0, 0);
 }
 
 template <int KV, int D, int BS>
 __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int num_qtiles,
                                                               int num_pairs) {
-  constexpr int kKStride = D * 2 + 16;       // bytes per key row of K in LDS
-  constexpr int kKSteps = D / 16;            // S^T contraction steps
-  constexpr int kDBlocks = D / 32;           // O^T row blocks
-  constexpr int kKBytes = kBN * kKStride;
-  constexpr int kVBytes = D * kVtStride;
-  constexpr int kKChunks = kBN * D / 8;      // 16-byte chunks of a K tile
-  constexpr int kVItems = (kBN / 2) * (D / 8);  // (key pair, 8 dims) items of a V tile
-  constexpr int kKPer = (kKChunks + 255) / 256;
-  constexpr int kVPer = (kVItems + 255) / 256;
-  static_assert(kBN % BS == 0 || BS > kBN, "tile / block");
+  constexpr int kRowBytes = D * 2;
+  constexpr int kChunks = D / 8;                       // 16-byte chunks per row
+  constexpr int kTileBytes = kBN * kRowBytes;
+  constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB wave-loads per wave
+  constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  constexpr int kBlocksPerLoad = kRowsPerLoad > BS ? kRowsPerLoad / BS : 1;
+  constexpr int kOpsPerTile = 2 * kLoadsPerWave;       // vector-memory ops per tile (K + V)
+  constexpr int kKSteps = D / 16;
+  constexpr int kDBlocks = D / 32;
+  constexpr int kP = kPrefetch;                        // tiles in flight ahead
+  static_assert(kLoadsPerWave >= 1 && kBlocksPerLoad <= 2, "tile geometry");
 
-  __shared__ __attribute__((aligned(16))) char lds[2][kKBytes + kVBytes];
+  // Three-stage rings (tiles t, t+1, t+2) of K tiles, raw V tiles and fp16
+  // V^T tiles, each stage its own array: the stage is a compile-time
+  // constant in every access (the loop is unrolled by three), so the
+  // compiler can tell that a DMA still in flight writes another stage than
+  // the one being read and does not wait for it.  Rows are 16-byte-chunk
+  // XOR-swizzled so that fragment reads do not collide on banks: K row r
+  // keeps chunk c at c ^ swz_k(r), V at c ^ swz_v(r).
+  static_assert(kP == 2, "three-stage rings");
+  __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes], lds_k1[kTileBytes],
+      lds_k2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes], lds_v1[kTileBytes],
+      lds_v2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lds_vt0[D * kVtStride], lds_vt1[D * kVtStride],
+      lds_vt2[D * kVtStride];
+  auto stage_k = [&](auto st) -> char* {
+    if constexpr (decltype(st)::value == 0) return lds_k0;
+    else if constexpr (decltype(st)::value == 1) return lds_k1;
+    else return lds_k2;
+  };
+  auto stage_v = [&](auto st) -> char* {
+    if constexpr (decltype(st)::value == 0) return lds_v0;
+    else if constexpr (decltype(st)::value == 1) return lds_v1;
+    else return lds_v2;
+  };
+  auto stage_vt = [&](auto st) -> char* {
+    if constexpr (decltype(st)::value == 0) return lds_vt0;
+    else if constexpr (decltype(st)::value == 1) return lds_vt1;
+    else return lds_vt2;
+  };
+  auto swz_k = [](int r) { return (r * kChunks / 16) % kChunks; };
+  auto swz_v = [](int r) { return (r / 2) % kChunks; };
 
   // Work item: (pair = seq * H + head, query tile); pairs are dealt to XCDs
   // round robin by pair, the query tiles of a pair go to the same XCD, last
@@ -134,74 +200,65 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
       qf[kk] = ok ? *(const uint4*)(qrow + kk * 16 + 8 * half) : make_uint4(0, 0, 0, 0);
   }
 
-  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
-  const int64_t tile_elems = int64_t(BS) * D;
+  // The block table is read-only during the kernel: read it through the
+  // constant address space so that the uniform lookups below are scalar
+  // loads (a vector load here would make the wait for it also wait for every
+  // DMA issued before it).
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* table = (const_i32*)(a.block_tables + int64_t(seq) * a.max_blocks_per_seq);
+  const int last_idx = (L - 1) / BS;
+  const int64_t last_blk = table[last_idx];
+  const int64_t head_off = int64_t(head) * BS * D;      // elements
+  const int64_t blk_stride = int64_t(H) * BS * D;
   const uint16_t* kpool = (const uint16_t*)a.k_cache;
   const uint16_t* vpool = (const uint16_t*)a.v_cache;
 
-  // Global -> register staging of one KV tile.
-  uint4 kreg[kKPer], vreg[kVPer][2];
-  auto load_tile = [&](int t) {
+  // DMA of tile t into K stage dk and V stage dv.  Keys past the sequence
+  // end re-read its last key (finite data; those keys are masked).
+  auto dma_tile = [&](int t, char* dk, char* dv) {
     const int kb = t * kBN;
 #pragma unroll
-    for (int i = 0; i < kKPer; ++i) {
-      const int c = tid + i * 256;
-      const int key = c / (D / 8);
-      const int dc = c % (D / 8);
-      const int kabs = kb + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < kKChunks && kabs < L) {
-        const int64_t blk = table[kabs / BS];
-        v = *(const uint4*)(kpool + (blk * H + head) * tile_elems + (kabs % BS) * D + dc * 8);
-      }
-      kreg[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < kVPer; ++i) {
-      const int w = tid + i * 256;
-      const int kp = w % (kBN / 2);
-      const int dc = w / (kBN / 2);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int kabs = kb + 2 * kp + e;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (w < kVItems && kabs < L) {
-          const int64_t blk = table[kabs / BS];
-          v = *(const uint4*)(vpool + (blk * H + head) * tile_elems + (kabs % BS) * D + dc * 8);
-        }
-        vreg[i][e] = v;
-      }
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int li = wave * kLoadsPerWave + i;
+      const int row0 = li * kRowsPerLoad;
+      const int b0 = __builtin_amdgcn_readfirstlane((kb + row0) / BS);
+      const int64_t blk_a = table[__builtin_amdgcn_readfirstlane(min(b0, last_idx))];
+      const int64_t blk_b =
+          kBlocksPerLoad > 1 ? table[__builtin_amdgcn_readfirstlane(min(b0 + 1, last_idx))] : blk_a;
+      const int row = row0 + lane / kChunks;
+      const int pos = lane % kChunks;
+      const int key = kb + row;
+      const bool in = key < L;
+      const int keyc = in ? key : L - 1;
+      const int64_t blk = in ? (key / BS == b0 ? blk_a : blk_b) : last_blk;
+      const int64_t e = blk * blk_stride + head_off + int64_t(keyc % BS) * D;
+      load_lds16(kpool + e + (pos ^ swz_k(row)) * 8, dk + li * 1024);
+      load_lds16(vpool + e + (pos ^ swz_v(row)) * 8, dv + li * 1024);
     }
   };
-  auto store_tile = [&](int buf) {
-    char* kl = lds[buf];
-    char* vl = lds[buf] + kKBytes;
+
+  // Raw V stage vr -> V^T stage vt (fp16, dimension-major, keys paired).
+  auto transpose_v = [&](const char* vr, char* vt) {
 #pragma unroll
-    for (int i = 0; i < kKPer; ++i) {
-      const int c = tid + i * 256;
-      if (c < kKChunks) {
-        const int key = c / (D / 8);
-        const int dc = c % (D / 8);
-        *(uint4*)(kl + key * kKStride + dc * 16) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kVPer; ++i) {
-      const int w = tid + i * 256;
-      if (w < kVItems) {
+    for (int w0 = 0; w0 < (kBN / 2) * kChunks; w0 += kWaves * 64) {
+      const int w = w0 + tid;
+      if (w < (kBN / 2) * kChunks) {
         const int kp = w % (kBN / 2);
         const int dc = w / (kBN / 2);
-        const uint32_t a0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-        const uint32_t a1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
+        const int r0 = 2 * kp, r1 = 2 * kp + 1;
+        const uint4 x = *(const uint4*)(vr + r0 * kRowBytes + (dc ^ swz_v(r0)) * 16);
+        const uint4 y = *(const uint4*)(vr + r1 * kRowBytes + (dc ^ swz_v(r1)) * 16);
+        const uint32_t a0[4] = {x.x, x.y, x.z, x.w};
+        const uint32_t a1[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t x = to_f16x2<KV>(a0[j]);  // key 2kp: dims 2j, 2j+1
-          const uint32_t y = to_f16x2<KV>(a1[j]);  // key 2kp+1
-          const uint32_t lo = (x & 0xffffu) | (y << 16);          // dim 2j: keys 2kp, 2kp+1
-          const uint32_t hi = (x >> 16) | (y & 0xffff0000u);      // dim 2j+1
+          // a0[j]: key 2kp, dims 2j and 2j+1; a1[j]: key 2kp+1.  Regroup by
+          // dimension (keys 2kp, 2kp+1 side by side), then convert to fp16.
+          const uint32_t lo = to_f16x2<KV>(interleave_lo(a0[j], a1[j]));  // dim 2j
+          const uint32_t hi = to_f16x2<KV>(interleave_hi(a0[j], a1[j]));  // dim 2j+1
           const int d = dc * 8 + 2 * j;
-          *(uint32_t*)(vl + d * kVtStride + kp * 4) = lo;
-          *(uint32_t*)(vl + (d + 1) * kVtStride + kp * 4) = hi;
+          *(uint32_t*)(vt + d * kVtStride + kp * 4) = lo;
+          *(uint32_t*)(vt + (d + 1) * kVtStride + kp * 4) = hi;
         }
       }
     }
@@ -216,65 +273,99 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
   const int my_row = wq0 + col;           // query row of this lane's column
   const int my_lim = ctx + my_row;        // last key it sees
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // Prologue: tiles 0 and 1 in flight (past the last tile, the last again).
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  dma_tile(0, stage_k(S0{}), stage_v(S0{}));
+  dma_tile(min(1, n_tiles - 1), stage_k(S1{}), stage_v(S1{}));
+  __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile 0 landed
+  __builtin_amdgcn_s_barrier();
+  transpose_v(stage_v(S0{}), stage_vt(S0{}));
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+  // One tile: issue tile t+2 (stage st+2), consume tile t (stage st), then
+  // build tile t+1's V^T (stage st+1) once tile t+1 has landed.  Every
+  // iteration issues exactly one tile's DMA, so the waits are exact.
+  auto iter = [&](auto st, int t) {
+    constexpr int s0 = decltype(st)::value;
+    using Sn = std::integral_constant<int, (s0 + 1) % 3>;
+    using Snn = std::integral_constant<int, (s0 + 2) % 3>;
     const int kb = t * kBN;
-    if (kb <= wave_last_key) {
-      const char* kl = lds[buf];
-      const char* vl = lds[buf] + kKBytes;
+    const bool active = kb <= wave_last_key;
+    const char* kl = stage_k(st);
+    auto kfrag = [&](int kk) {
+      return *(const uint4*)(kl + col * kRowBytes + ((2 * kk + half) ^ swz_k(col)) * 16);
+    };
+    // The first LDS read of the tile comes before the next DMA is issued:
+    // where the compiler cannot tell which stage an in-flight DMA writes
+    // (the loop header) it waits for all of them, and at this point that is
+    // only tile t+1, issued an iteration ago.
+    const uint4 kf0 = active ? kfrag(0) : make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_tile(min(t + 2, n_tiles - 1), stage_k(Snn{}), stage_v(Snn{}));
+    __builtin_amdgcn_sched_barrier(0);
+    if (active) {
+      const char* vl = stage_vt(st);
       // S^T = K Q^T : rows = keys of the tile, columns = this wave's queries.
       f32x16_t s;
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = 0.f;
+      s = mfma_qk<KV>(kf0, qf[0], s);
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        const uint4 kf = *(const uint4*)(kl + col * kKStride + kk * 32 + half * 16);
-        s = mfma_qk<KV>(kf, qf[kk], s);
-      }
+      for (int kk = 1; kk < kKSteps; ++kk) s = mfma_qk<KV>(kfrag(kk), qf[kk], s);
       // Register v of this lane holds key 8*(v/4) + 4*half + v%4 of the tile.
-      const bool crosses = kb + kBN - 1 > ctx + wq0;
-      float mx = kNoMax;
+      // Scores stay unscaled here; c = scale*log2(e) > 0 is folded into the
+      // exponent below.
+      // The scores are copied out of the accumulator once and never written
+      // back (edits in place would make the compiler move the accumulator
+      // between register files on every tile).
+      const float c = a.scale_log2;
+      float x[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = s[v] * a.scale_log2;
-        if (crosses) {
+      for (int v = 0; v < 16; ++v) x[v] = s[v];
+      if (kb + kBN - 1 > ctx + wq0) {  // the tile crosses the causal diagonal
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
           const int key = kb + 8 * (v / 4) + 4 * half + (v % 4);
-          x = key <= my_lim ? x : -INFINITY;
+          x[v] = key <= my_lim ? x[v] : -INFINITY;
         }
-        s[v] = x;
-        mx = fmaxf(mx, x);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      float mx = x[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      // Rows whose maximum grew past the slack move their reference maximum.
+      // The branch is taken for the whole wave (a vote), so the accumulators
+      // are touched only on the rare tiles where some row needs it.
+      const bool moves = mx > m + kRescaleSlack;
+      if (__any(moves)) {
+        const float m_new = moves ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+        m = m_new;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        s[v] = __builtin_amdgcn_exp2f(s[v] - m_new);
-        psum += s[v];
+        x[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, -m));
+        psum += x[v];
       }
-      l = fmaf(l, alpha, psum);
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      l += psum;
       // P^T as B operands: k-step tt takes accumulator registers 8tt .. 8tt+7,
       // i.e. keys 16tt + 8*(e/4) + 4*half + e%4 for e = 0..7.
       uint4 pf[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        pf[tt] = make_uint4(pack_f16(s[8 * tt + 0], s[8 * tt + 1]),
-                            pack_f16(s[8 * tt + 2], s[8 * tt + 3]),
-                            pack_f16(s[8 * tt + 4], s[8 * tt + 5]),
-                            pack_f16(s[8 * tt + 6], s[8 * tt + 7]));
+        pf[tt] = make_uint4(pack_f16(x[8 * tt + 0], x[8 * tt + 1]),
+                            pack_f16(x[8 * tt + 2], x[8 * tt + 3]),
+                            pack_f16(x[8 * tt + 4], x[8 * tt + 5]),
+                            pack_f16(x[8 * tt + 6], x[8 * tt + 7]));
       // O^T += V^T P^T : A = V^T rows (dims) with the same key order.
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
@@ -287,9 +378,25 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
         }
       }
     }
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile t+1 landed
+    __builtin_amdgcn_s_barrier();
+    if (t + 1 < n_tiles) transpose_v(stage_v(Sn{}), stage_vt(Sn{}));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+  };
+  // The first iteration is peeled so that both edges into the loop come
+  // from the same stage (the same DMA in flight): the compiler's view of
+  // outstanding LDS writes then stays exact across the back edge.
+  iter(S0{}, 0);
+  for (int t = 1; t < n_tiles;) {
+    iter(S1{}, t);
+    if (++t >= n_tiles) break;
+    iter(S2{}, t);
+    if (++t >= n_tiles) break;
+    iter(S0{}, t);
+    ++t;
   }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // Normalise and store: lane holds query my_row, dims 8*(v/4) + 4*half + v%4.
   l += __shfl_xor(l, 32);
