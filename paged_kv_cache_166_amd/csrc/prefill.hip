@@ -213,10 +213,38 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
   const uint16_t* kpool = (const uint16_t*)a.k_cache;
   const uint16_t* vpool = (const uint16_t*)a.v_cache;
 
-  // DMA of tile t into K stage dk and V stage dv.  Keys past the sequence
-  // end re-read its last key (finite data; those keys are masked).
+  // Inside a tile a lane always loads the same row-in-block and chunk (tiles
+  // start at multiples of the block size), so its byte offset from the
+  // (block, head) base is fixed: only the block id changes from tile to tile.
+  uint32_t off_k[kLoadsPerWave], off_v[kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int row = (wave * kLoadsPerWave + i) * kRowsPerLoad + lane / kChunks;
+    const int pos = lane % kChunks;
+    off_k[i] = uint32_t(((row % BS) * D + (pos ^ swz_k(row)) * 8) * 2);
+    off_v[i] = uint32_t(((row % BS) * D + (pos ^ swz_v(row)) * 8) * 2);
+  }
+  const int64_t tile_stride = int64_t(H) * BS * D * 2;   // bytes between blocks
+  const char* kbase0 = (const char*)a.k_cache + int64_t(head) * BS * D * 2;
+  const char* vbase0 = (const char*)a.v_cache + int64_t(head) * BS * D * 2;
+
+  // DMA of tile t into K stage dk and V stage dv.
   auto dma_tile = [&](int t, char* dk, char* dv) {
     const int kb = t * kBN;
+    if (kBlocksPerLoad == 1 && kb + kBN <= L) {
+      // Whole tile inside the sequence: one block per wave-load, uniform base.
+#pragma unroll
+      for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int li = wave * kLoadsPerWave + i;
+        const int64_t blk = table[__builtin_amdgcn_readfirstlane((kb + li * kRowsPerLoad) / BS)];
+        load_lds16(kbase0 + blk * tile_stride + off_k[i], dk + li * 1024);
+        load_lds16(vbase0 + blk * tile_stride + off_v[i], dv + li * 1024);
+      }
+      return;
+    }
+    // The tile reaches past the sequence end (or spans two blocks per
+    // wave-load): per-lane addresses; keys past the end re-read the last key
+    // (finite data; those keys are masked).
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
       const int li = wave * kLoadsPerWave + i;
