@@ -133,7 +133,8 @@ class DecodeBench:
     are), then, per layer, the cache write of the step's K/V into that
     layer's pool and pa_decode over it."""
 
-    def __init__(self, workload, steps, warmup, device, partition_blocks=None, layers=None):
+    def __init__(self, workload, steps, warmup, device, partition_blocks=None, layers=None,
+                 stream_kv=None):
         self.name = workload
         cfg = W.CONFIGS[workload]
         self.cfg = cfg
@@ -166,6 +167,9 @@ class DecodeBench:
             raise ValueError(workload)
         if partition_blocks is not None:
             self.pb = partition_blocks
+        # the pools' stream flag: only when no block is shared by two sequences
+        # (every workload but the shared-prefix one)
+        self.stream_kv = (workload != "prefix_cow") if stream_kv is None else stream_kv
         self.lens0 = lens0
         self.alloc = pa.Allocator(self.N, self.bs, W.free_order(cfg["seed"], self.N))
         g = torch.Generator(device=device)
@@ -204,7 +208,8 @@ class DecodeBench:
         self.cows = 0
 
     def _filled_pool(self, g):
-        pool = pa.PagedPool.empty(self.N, self.H, self.bs, self.D, self.kv, self.device)
+        pool = pa.PagedPool.empty(self.N, self.H, self.bs, self.D, self.kv, self.device,
+                                  stream_kv=self.stream_kv)
         for t in (pool.k_cache, pool.v_cache):
             for i in range(0, self.N, 1024):
                 n = min(1024, self.N - i)
@@ -235,10 +240,11 @@ class DecodeBench:
                 pa.pa_copy_blocks(pool, pairs)
             pa.pa_reshape_and_cache(pool, self.knew[(k + li) % 4], self.vnew[(k + li) % 4],
                                     d["slots"].view(-1))
-            # one launch per step (layer 0) carries the event pair: an event
-            # record waits for the caches to be written back, which would
-            # otherwise stall every layer
-            timing = timed and li == 0
+            # one launch per step carries the event pair (an event record
+            # waits for the caches to be written back, which would otherwise
+            # stall every layer): a middle layer, in the steady state -- the
+            # first layer after the step's upload runs a few us slower
+            timing = timed and li == len(self.pools) // 2
             if timing:
                 tm = Timer()
                 tm.start()
@@ -277,6 +283,7 @@ class DecodeBench:
             d["context_lens"] = f"uniform[{c['len_lo']},{c['len_hi']}] seed {c['seed']}"
         d["partition_blocks"] = self.pb or pa.pa_decode_auto_partition_blocks(self.pool, self.B,
                                                                               self.maxb)
+        d["stream_kv"] = self.stream_kv
         return d
 
     def cpu_baseline(self, budget_s=10.0):
@@ -444,6 +451,8 @@ def main():
     ap.add_argument("--partition-blocks", type=int, default=None,
                     help="decode split-K partition size in blocks (default: the library's choice, "
                          "or the workload's own)")
+    ap.add_argument("--stream-kv", choices=["auto", "on", "off"], default="auto",
+                    help="decode pools' PA_POOL_STREAM_KV flag (auto: on unless blocks are shared)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -466,7 +475,7 @@ def main():
         b = PrefillBench(args.steps, args.warmup, device)
     else:
         b = DecodeBench(args.workload, args.steps, args.warmup, device, args.partition_blocks,
-                        args.layers)
+                        args.layers, {"auto": None, "on": True, "off": False}[args.stream_kv])
     torch.cuda.synchronize()
     for k in range(args.warmup):
         b.step(k, False)

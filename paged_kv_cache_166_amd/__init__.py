@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_SEQ = 0, -1, -2, -3, -4, -5
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+PA_POOL_STREAM_KV = 1
 
 _DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
           torch.float8_e4m3fn: PA_FP8_E4M3}
@@ -48,7 +49,7 @@ class _Pool(ctypes.Structure):
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 def _load():
@@ -136,7 +137,8 @@ class PagedPool:
     scale per (block, head) for K and for V.
     """
 
-    def __init__(self, k_cache, v_cache, k_scale=None, v_scale=None, kv_dtype=None):
+    def __init__(self, k_cache, v_cache, k_scale=None, v_scale=None, kv_dtype=None,
+                 stream_kv=False):
         assert k_cache.shape == v_cache.shape and k_cache.dim() == 4
         assert k_cache.is_contiguous() and v_cache.is_contiguous()
         self.k_cache, self.v_cache = k_cache, v_cache
@@ -149,7 +151,17 @@ class PagedPool:
         self._struct = _Pool(k_cache.data_ptr(), v_cache.data_ptr(),
                              k_scale.data_ptr() if k_scale is not None else 0,
                              v_scale.data_ptr() if v_scale is not None else 0,
-                             N, H, bs, D, kv_dtype)
+                             N, H, bs, D, kv_dtype, PA_POOL_STREAM_KV if stream_kv else 0)
+
+    @property
+    def stream_kv(self):
+        """True: no block is shared by two sequences of a decode batch, so
+        pa_decode may stream K/V past the caches (PA_POOL_STREAM_KV)."""
+        return bool(self._struct.flags & PA_POOL_STREAM_KV)
+
+    @stream_kv.setter
+    def stream_kv(self, on):
+        self._struct.flags = (self._struct.flags & ~PA_POOL_STREAM_KV) | (PA_POOL_STREAM_KV if on else 0)
 
     @property
     def device(self):
@@ -159,7 +171,8 @@ class PagedPool:
         return ctypes.byref(self._struct)
 
     @staticmethod
-    def empty(num_blocks, num_heads, block_size, head_dim, kv_dtype, device, fill=None):
+    def empty(num_blocks, num_heads, block_size, head_dim, kv_dtype, device, fill=None,
+              stream_kv=False):
         """Allocate a pool (and fp8 scales of 1.0)."""
         tdt = torch.uint8 if kv_dtype == "fp8" else TORCH_DTYPE[kv_dtype]
         shape = (num_blocks, num_heads, block_size, head_dim)
@@ -172,7 +185,7 @@ class PagedPool:
         if kv_dtype == "fp8":
             ks = torch.ones((num_blocks, num_heads), dtype=torch.float32, device=device)
             vs = torch.ones((num_blocks, num_heads), dtype=torch.float32, device=device)
-        return PagedPool(k, v, ks, vs, _NAME[kv_dtype])
+        return PagedPool(k, v, ks, vs, _NAME[kv_dtype], stream_kv=stream_kv)
 
 
 # ---------------------------------------------------------------- GPU calls

@@ -29,6 +29,7 @@ pa_status check_pool(const char* fn, const pa_pool* p) {
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", fn, p->head_dim);
   if (!valid_dtype(p->kv_dtype)) return fail(PA_ERR_INVALID, "%s: kv_dtype %d", fn, p->kv_dtype);
+  if (p->flags & ~PA_POOL_STREAM_KV) return fail(PA_ERR_INVALID, "%s: unknown pool flags 0x%x", fn, p->flags);
   if (p->kv_dtype == PA_FP8_E4M3) {
     if (!p->k_scale || !p->v_scale) return fail(PA_ERR_INVALID, "%s: fp8 pool without scales", fn);
   }
@@ -181,7 +182,8 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
   return hip_status(fn, pa::launch_decode(a, pool->kv_dtype, pool->head_dim, pool->block_size,
-                                          num_seqs, stream));
+                                          (pool->flags & PA_POOL_STREAM_KV) != 0, num_seqs,
+                                          stream));
 }
 
 pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,

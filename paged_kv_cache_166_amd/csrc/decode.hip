@@ -23,6 +23,10 @@
 //    inside the group with DPP, and each group keeps its own running max and
 //    sum (online softmax) over the rows it sees -- no cross-group traffic in
 //    the loop;
+//  * with the pool's stream flag (no block shared by two sequences of the
+//    batch) V is read with non-temporal loads, which skip the cache fills a
+//    read-once stream does not need; K keeps ordinary loads (measured: one
+//    stream non-temporal beats both, and shared blocks want both cached);
 //  * the next block's K and V loads are issued before the current block is
 //    consumed (two register buffers), unconditionally: past the wave's last
 //    block they re-read that block (an L2 hit), so the number of loads in
@@ -176,7 +180,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr int kMaxPartBlocks = 256;
 
-template <int KV, int D, int BS, int NW>
+template <int KV, int D, int BS, int NW, bool kStreamV>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using G = Geo<KV, D, BS>;
   using Ops = KvOps<KV>;
@@ -194,8 +198,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int L = a.context_lens[seq];
+  // The block-table row and q do not depend on the context length: their
+  // loads go out together with it, so a workgroup waits for one round trip
+  // before it can address its first tile, not two.  Lane t of wave w reads
+  // entry w + NW t of the partition (bounded by the table's row length; the
+  // entries past the sequence's blocks are never used).
   const int64_t out_off = (int64_t(seq) * H + head) * D;
+  const int blk0 = part * a.part_blocks;
+  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq + blk0;
+  const int t_idx = wave + NW * lane;
+  const int tab = (t_idx < a.part_blocks && blk0 + t_idx < a.max_blocks_per_seq) ? table[t_idx] : 0;
+  static_assert(kMaxPartBlocks <= 64 * NW, "one table register per wave");
+  const int grp = lane / G::kLpr;
+  const int col = lane % G::kLpr;
+  const typename Ops::Q q = Ops::load_q(a.q, out_off + col * E, a.q_dtype);
+
+  const int L = a.context_lens[seq];
   if (L <= 0) {
     if (part == 0)
       for (int d = tid; d < D; d += NW * 64) store_from_f32(a.out, out_off + d, a.out_dtype, 0.f);
@@ -204,21 +222,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int nblocks = (L + BS - 1) / BS;
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
   if (part >= nparts) return;
-  const int blk0 = part * a.part_blocks;
   const int nb = min(a.part_blocks, nblocks - blk0);
-
-  const int grp = lane / G::kLpr;
-  const int col = lane % G::kLpr;
   const bool row_ok = !G::kIdleGroups || grp < BS;
 
   // This wave's blocks are wave, wave + NW, ... of the partition (n_w <= 64
-  // of them); lane t holds the block id of the wave's t-th block.
+  // of them); lane t of `tab` holds the block id of the wave's t-th block.
   const int n_w = wave < nb ? (nb - wave + NW - 1) / NW : 0;
-  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq + blk0;
-  const int tab = lane < n_w ? table[wave + NW * lane] : 0;
-  static_assert(kMaxPartBlocks <= 64 * NW, "one table register per wave");
-
-  const typename Ops::Q q = Ops::load_q(a.q, out_off + col * E, a.q_dtype);
   const int64_t blk_stride = int64_t(H) * G::kTileBytes;
   const char* kbase = (const char*)a.k_cache + int64_t(head) * G::kTileBytes + lane * 16;
   const char* vbase = (const char*)a.v_cache + int64_t(head) * G::kTileBytes + lane * 16;
@@ -239,7 +248,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (int i = 0; i < G::kLoads; ++i) {
       if (row_ok) {
         kr[i] = *(const uint4*)(kp + i * 1024);
-        vr[i] = *(const uint4*)(vp + i * 1024);
+        if constexpr (kStreamV) {
+          const u32x4_t x = __builtin_nontemporal_load((const u32x4_t*)(vp + i * 1024));
+          vr[i] = make_uint4(x.x, x.y, x.z, x.w);
+        } else {
+          vr[i] = *(const uint4*)(vp + i * 1024);
+        }
       } else {
         kr[i] = make_uint4(0, 0, 0, 0);
         vr[i] = make_uint4(0, 0, 0, 0);
@@ -368,16 +382,31 @@ __global__ __launch_bounds__(D * R) void decode_merge_kernel(DecodeArgs a) {
   const int H = a.num_heads;
   const int d = threadIdx.x % D;
   const int r = threadIdx.x / D;
+  const int64_t sh = int64_t(seq) * H + head;
+  const float* ml = a.ws_ml + 2 * sh * a.max_parts;
+  const float* pa = a.ws_acc + sh * a.max_parts * D + d;
+  // Partition r's triple is loaded before the context length is known (it
+  // lies inside the workspace whenever r < max_parts, and is used only if
+  // the partition exists), so the common case of at most R partitions waits
+  // for one round trip to memory, not two.
+  float m0 = kNoMax, l0 = 0.f, x0 = 0.f;
+  if (r < a.max_parts) {
+    m0 = ml[2 * r];
+    l0 = ml[2 * r + 1];
+    x0 = pa[int64_t(r) * D];
+  }
   const int L = a.context_lens[seq];
   const int nblocks = (L + a.block_size - 1) / a.block_size;
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
   if (nparts <= 1) return;
-  const int64_t sh = int64_t(seq) * H + head;
-  const float* ml = a.ws_ml + 2 * sh * a.max_parts;
-  const float* pa = a.ws_acc + sh * a.max_parts * D + d;
   float M = kNoMax, A = 0.f, S = 0.f;
+  if (r < nparts) {
+    M = m0;
+    S = l0;
+    A = x0;
+  }
 #pragma unroll 4
-  for (int p = r; p < nparts; p += R) {
+  for (int p = r + R; p < nparts; p += R) {
     const float m = ml[2 * p], l = ml[2 * p + 1], x = pa[int64_t(p) * D];
     const float Mn = fmaxf(M, m);
     const float fo = fast_exp2(M - Mn), fn = fast_exp2(m - Mn);
@@ -407,9 +436,14 @@ __global__ __launch_bounds__(D * R) void decode_merge_kernel(DecodeArgs a) {
 constexpr int kWaves = 4;
 
 template <int KV, int D, int BS>
-hipError_t launch_t(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
+hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_t stream) {
   dim3 grid(a.num_heads, num_seqs, a.max_parts);
-  hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, a);
+  if (stream_v)
+    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true>), grid, dim3(kWaves * 64), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false>), grid, dim3(kWaves * 64), 0,
+                       stream, a);
   constexpr int R = 512 / D;
   if (a.max_parts > 1)
     hipLaunchKernelGGL((decode_merge_kernel<D, R>), dim3(a.num_heads, num_seqs), dim3(D * R), 0,
@@ -418,32 +452,35 @@ hipError_t launch_t(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
 }
 
 template <int KV, int D>
-hipError_t launch_bs(const DecodeArgs& a, int bs, int num_seqs, hipStream_t stream) {
+hipError_t launch_bs(const DecodeArgs& a, int bs, bool sv, int num_seqs, hipStream_t stream) {
   switch (bs) {
-    case 4: return launch_t<KV, D, 4>(a, num_seqs, stream);
-    case 8: return launch_t<KV, D, 8>(a, num_seqs, stream);
-    case 16: return launch_t<KV, D, 16>(a, num_seqs, stream);
-    case 32: return launch_t<KV, D, 32>(a, num_seqs, stream);
+    case 4: return launch_t<KV, D, 4>(a, sv, num_seqs, stream);
+    case 8: return launch_t<KV, D, 8>(a, sv, num_seqs, stream);
+    case 16: return launch_t<KV, D, 16>(a, sv, num_seqs, stream);
+    case 32: return launch_t<KV, D, 32>(a, sv, num_seqs, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KV>
-hipError_t launch_d(const DecodeArgs& a, int d, int bs, int num_seqs, hipStream_t stream) {
-  if (d == 64) return launch_bs<KV, 64>(a, bs, num_seqs, stream);
-  if (d == 128) return launch_bs<KV, 128>(a, bs, num_seqs, stream);
+hipError_t launch_d(const DecodeArgs& a, int d, int bs, bool sv, int num_seqs,
+                    hipStream_t stream) {
+  if (d == 64) return launch_bs<KV, 64>(a, bs, sv, num_seqs, stream);
+  if (d == 128) return launch_bs<KV, 128>(a, bs, sv, num_seqs, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
-                         int num_seqs, hipStream_t stream) {
+                         bool stream_v, int num_seqs, hipStream_t stream) {
+  const int d = head_dim, bs = block_size;
+  const bool sv = stream_v;
   switch (kv_dtype) {
-    case PA_F32: return launch_d<PA_F32>(a, head_dim, block_size, num_seqs, stream);
-    case PA_F16: return launch_d<PA_F16>(a, head_dim, block_size, num_seqs, stream);
-    case PA_BF16: return launch_d<PA_BF16>(a, head_dim, block_size, num_seqs, stream);
-    case PA_FP8_E4M3: return launch_d<PA_FP8_E4M3>(a, head_dim, block_size, num_seqs, stream);
+    case PA_F32: return launch_d<PA_F32>(a, d, bs, sv, num_seqs, stream);
+    case PA_F16: return launch_d<PA_F16>(a, d, bs, sv, num_seqs, stream);
+    case PA_BF16: return launch_d<PA_BF16>(a, d, bs, sv, num_seqs, stream);
+    case PA_FP8_E4M3: return launch_d<PA_FP8_E4M3>(a, d, bs, sv, num_seqs, stream);
   }
   return hipErrorInvalidValue;
 }

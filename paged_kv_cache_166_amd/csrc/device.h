@@ -12,6 +12,7 @@ namespace pa {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 // Running maximum before any key: finite, so exp2(m - m_new) never sees

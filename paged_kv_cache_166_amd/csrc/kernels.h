@@ -29,7 +29,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
-                         int num_seqs, hipStream_t stream);
+                         bool stream_v, int num_seqs, hipStream_t stream);
 
 struct CacheWriteArgs {
   void* k_cache;

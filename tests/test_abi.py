@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import paged_kv_cache_166_amd as pa
 
@@ -50,10 +51,22 @@ def _decode(pool, **kw):
     ("num_blocks", 0, pa.PA_ERR_INVALID),
     ("k_cache", 0x10040, pa.PA_ERR_INVALID),      # not 128-byte aligned
     ("k_cache", 0, pa.PA_ERR_INVALID),
+    ("flags", 2, pa.PA_ERR_INVALID),               # unknown pool flag
 ])
 def test_pool_checks(field, value, code):
     assert _decode(_fake_pool(**{field: value})) == code
     assert pa.lib.pa_last_error()
+
+
+def test_pool_stream_flag_is_accepted():
+    p = _fake_pool(flags=pa.PA_POOL_STREAM_KV)
+    assert _decode(p, B=0) == pa.PA_OK
+    assert _decode(p, q_dtype=pa.PA_BF16) == pa.PA_ERR_UNSUPPORTED   # other checks still apply
+    kv = torch.empty((2, 1, 4, 64), dtype=torch.float16)
+    pool = pa.PagedPool(kv, kv)
+    assert not pool.stream_kv
+    pool.stream_kv = True
+    assert pool._struct.flags == pa.PA_POOL_STREAM_KV and pool.stream_kv
 
 
 def test_decode_argument_checks_before_launch():

@@ -84,6 +84,14 @@ def test_decode_sweep(kv, D, bs):
         got, _, _ = _run_decode(sc, seqs, q_dev, scale, pb)
         assert_close(got, ref, TOL[kv], f"{kv} D={D} bs={bs} pb={pb}")
         assert np.all(got[0] == 0.0)                      # empty sequence -> zeros
+    # the pool's stream flag changes only the cache policy of the V loads:
+    # bit-identical results
+    for pb in (0, 3):
+        plain, _, _ = _run_decode(sc, seqs, q_dev, scale, pb)
+        sc.pool.stream_kv = True
+        streamed, _, _ = _run_decode(sc, seqs, q_dev, scale, pb)
+        sc.pool.stream_kv = False
+        assert np.array_equal(plain.view(np.uint32), streamed.view(np.uint32)), f"stream pb={pb}"
     if qdt != "f32":
         got, _, _ = _run_decode(sc, seqs, q_dev, scale, 3, out_dtype=pa.TORCH_DTYPE[qdt])
         tol = TOL[kv] + half_ulp(qdt, ref)
@@ -125,6 +133,9 @@ def test_llama13b_decode_workload():
         got, _, _ = _run_decode(sc, seqs, q_dev, scale, pb, max_blocks=2048 // 16)
         err = assert_close(got, ref, TOL["f16"], f"llama13b pb={pb}")
         print(f"llama13b pb={pb}: max abs err {err:.2e}, rel {err / np.abs(ref).max():.2e}")
+    sc.pool.stream_kv = True                 # as the benchmark runs it
+    got, _, _ = _run_decode(sc, seqs, q_dev, scale, 0, max_blocks=2048 // 16)
+    assert_close(got, ref, TOL["f16"], "llama13b streamed")
 
 
 def test_prefix_cow_workload():
@@ -216,6 +227,12 @@ def test_long_fp8_decode_workload():
         outs[pb] = out.cpu().numpy().astype(np.float64)
         assert np.all(np.isfinite(outs[pb]))
     assert np.max(np.abs(outs[16] - outs[64])) < 1e-5
+    pool.stream_kv = True                    # as the benchmark runs it: same bits
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    pa.pa_decode(out, q, pool, tables, lens, 1 / math.sqrt(D), 16,
+                 pa.decode_workspace(pool, B, L // bs, 16))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), outs[16])
     ks, vs = pool.k_scale.cpu().numpy(), pool.v_scale.cpu().numpy()
     q64 = q.float().cpu().numpy().astype(np.float64)
     for (s, h), (kx, vx) in kept.items():
