@@ -9,9 +9,9 @@
 // How: a workgroup of 4 wavefronts owns 128 query rows of one (sequence,
 // head); wave w owns 32 of them.  The keys are walked in tiles of 32 tokens
 // (one to eight blocks, found through the block table):
-//  * the K tile is staged in LDS as rows; the V tile is staged transposed
-//    (dimension-major) and converted to fp16; two LDS buffers, the next
-//    tile's global loads in flight while the current tile is consumed;
+//  * K and V tiles land in LDS as rows, by DMA (global_load_lds_dwordx4)
+//    into three-stage rings, two tiles in flight while one is consumed; one
+//    workgroup barrier per tile;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16 (bf16 or fp16 inputs, fp32
 //    accumulate): A = K rows from LDS, B = the wave's Q rows, held in
 //    registers for the whole walk;
@@ -20,10 +20,15 @@
 //    l, exp2 of log2-scaled scores) is lane-local plus one exchange between
 //    the two half-waves; a row's reference maximum (and so the accumulator
 //    rescale) moves only when the row maximum grows by more than 2^8;
-//  * O^T += V^T P^T on v_mfma_f32_32x32x16_f16: P (rounded to fp16) is used
-//    straight from the S^T accumulators as the B operand -- the contraction
-//    index is permuted to match the accumulator layout and V^T is read from
-//    LDS in the same permuted key order -- so P never leaves registers;
+//  * O^T += V^T P^T on v_mfma_f32_32x32x16: P is used straight from the S^T
+//    accumulators as the B operand (the contraction index is permuted to
+//    match the accumulator layout) so P never leaves registers; the V^T
+//    operand is read from the V rows by gfx950's transposing LDS read
+//    (ds_read_b64_tr_b16) in the same permuted key order.  P is rounded to
+//    fp16 (bf16's 8 bits would cost up to ~5e-3 on rows of a few keys); for
+//    bf16 pools each wave converts the V chunks its own DMA brought in to
+//    fp16 in place, once the DMA has landed and before the barrier that
+//    publishes the tile;
 //  * tiles wholly above the causal diagonal are skipped per wave; only
 //    tiles that cross it are masked.
 // Workgroups are mapped so that all query tiles of one (sequence, head) run
@@ -39,14 +44,12 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
 constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBM = kWaves * kQW;       // query rows per workgroup
 constexpr int kBN = 32;                 // keys per tile
-constexpr int kVtStride = 72;           // bytes per dimension row of V^T in LDS
 constexpr int kXcds = 8;
 constexpr int kPrefetch = 2;            // K/V tiles in flight ahead of the one consumed
 
@@ -73,19 +76,58 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
 }
 
-// Two 16-bit values of the pool's type -> packed fp16 pair (RNE).
-template <int KV>
-__device__ __forceinline__ uint32_t to_f16x2(uint32_t w) {
-  if constexpr (KV == PA_F16) return w;
-  return pack_f16(bf16_lo(w), bf16_hi(w));
+// Eight bf16 values -> eight fp16 values (RNE), in place in a 16-byte word.
+__device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t w) {
+  return u32x4_t{pack_f16(bf16_lo(w.x), bf16_hi(w.x)), pack_f16(bf16_lo(w.y), bf16_hi(w.y)),
+                 pack_f16(bf16_lo(w.z), bf16_hi(w.z)), pack_f16(bf16_lo(w.w), bf16_hi(w.w))};
 }
 
-// Low / high 16-bit halves of x and y side by side: (x.lo, y.lo), (x.hi, y.hi).
-__device__ __forceinline__ uint32_t interleave_lo(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16), 8 bytes per lane: in each
+// group of 16 lanes, lane i receives 16-bit element i % 4 of the 8-byte
+// pieces addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 (in that
+// order).  So if lane j addresses 4 consecutive dimensions d0 + 4 (j % 4) ..
+// of row r0 + j / 4, lane i gets dimension d0 + i of rows r0 .. r0 + 3.
+//
+// Issued as inline assembly with an immediate offset: the compiler's wait
+// insertion cannot tell the ring stages apart for this instruction and would
+// otherwise drain every DMA in flight before some of these reads.  The
+// caller waits with lds_wait_tr() before using the results.
+template <int kOffset>
+__device__ __forceinline__ uint2 lds_read_tr16(uint32_t lds_addr) {
+  static_assert(kOffset >= 0 && kOffset < 65536, "ds offset field");
+  uint2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(kOffset));
+  return r;
 }
-__device__ __forceinline__ uint32_t interleave_hi(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+
+// n 16-byte LDS reads at a, a + 1024, ... (inline assembly, waited for
+// before returning) and the matching writes (complete at the next wait for
+// LDS operations, such as the one in wg_barrier()).
+template <int n>
+__device__ __forceinline__ void lds_read_b128_x(uint32_t a, u32x4_t (&w)[n]) {
+  static_assert(n == 1 || n == 2, "one or two chunks per lane");
+  asm volatile("ds_read_b128 %0, %1" : "=v"(w[0]) : "v"(a));
+  if constexpr (n == 2) {
+    asm volatile("ds_read_b128 %0, %1 offset:1024" : "=v"(w[1]) : "v"(a));
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]));
+  }
+}
+template <int n>
+__device__ __forceinline__ void lds_write_b128_x(uint32_t a, const u32x4_t (&w)[n]) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(w[0]) : "memory");
+  if constexpr (n == 2) asm volatile("ds_write_b128 %0, %1 offset:1024" : : "v"(a), "v"(w[1]) : "memory");
+}
+
+// Wait for every LDS read issued so far (the transposing reads above among
+// them); the values pass through the statement so no use of them can be
+// scheduled before the wait.
+__device__ __forceinline__ void lds_wait_tr(uint2 (&v)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
 }
 
 // The running maximum a query row's weights are taken against moves only
@@ -97,10 +139,23 @@ constexpr float kRescaleSlack = 8.0f;
 // other counters unconstrained (vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
 // vmcnt[5:4] << 14).
 constexpr int wait_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
-// s_waitcnt immediate: all LDS / scalar-memory operations done.
-constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 
 typedef __attribute__((address_space(3))) void lds_t;
+
+// s_waitcnt immediate: all LDS / scalar-memory operations done, vector
+// memory unconstrained.
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+
+// Workgroup barrier without a memory fence: this wave's LDS accesses are
+// complete when it arrives, and the vector-memory waits before it are the
+// caller's (a fence would also wait for every DMA in flight); the empty asm
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // 16 bytes per lane from global memory straight into LDS (gfx950
 // global_load_lds_dwordx4): lane i's bytes land at dst + 16 i; dst is
@@ -109,9 +164,12 @@ __device__ __forceinline__ void load_lds16(const void* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_t*)dst, 16, 0, 0);
 }
 
+// At least three waves per SIMD (at most 168 VGPRs; 48 KiB of LDS fit three
+// workgroups per CU): the loop is latency-bound, and a third workgroup per
+// CU hides more of it than the registers the compiler gives up cost.
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int num_qtiles,
-                                                              int num_pairs) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   constexpr int kRowBytes = D * 2;
   constexpr int kChunks = D / 8;                       // 16-byte chunks per row
   constexpr int kTileBytes = kBN * kRowBytes;
@@ -124,20 +182,20 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
   constexpr int kP = kPrefetch;                        // tiles in flight ahead
   static_assert(kLoadsPerWave >= 1 && kBlocksPerLoad <= 2, "tile geometry");
 
-  // Three-stage rings (tiles t, t+1, t+2) of K tiles, raw V tiles and fp16
-  // V^T tiles, each stage its own array: the stage is a compile-time
-  // constant in every access (the loop is unrolled by three), so the
-  // compiler can tell that a DMA still in flight writes another stage than
-  // the one being read and does not wait for it.  Rows are 16-byte-chunk
-  // XOR-swizzled so that fragment reads do not collide on banks: K row r
-  // keeps chunk c at c ^ swz_k(r), V at c ^ swz_v(r).
+  // Three-stage rings (tiles t, t+1, t+2) of K and V tiles, each stage its
+  // own array: the stage is a compile-time constant in every access (the
+  // loop is unrolled by three), so the compiler can tell that a DMA still in
+  // flight writes another stage than the one being read and does not wait
+  // for it.  Rows are 16-byte-chunk XOR-swizzled so that fragment reads do
+  // not collide on banks: K row r keeps chunk c at c ^ swz_k(r), V at
+  // c ^ swz_v(r).  A transposing V read touches 4 chunks of each of 4
+  // consecutive rows per half-wave: swz_v moves those rows to distinct
+  // aligned groups of 4 chunks.
   static_assert(kP == 2, "three-stage rings");
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes], lds_k1[kTileBytes],
       lds_k2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes], lds_v1[kTileBytes],
       lds_v2[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char lds_vt0[D * kVtStride], lds_vt1[D * kVtStride],
-      lds_vt2[D * kVtStride];
   auto stage_k = [&](auto st) -> char* {
     if constexpr (decltype(st)::value == 0) return lds_k0;
     else if constexpr (decltype(st)::value == 1) return lds_k1;
@@ -148,13 +206,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
     else if constexpr (decltype(st)::value == 1) return lds_v1;
     else return lds_v2;
   };
-  auto stage_vt = [&](auto st) -> char* {
-    if constexpr (decltype(st)::value == 0) return lds_vt0;
-    else if constexpr (decltype(st)::value == 1) return lds_vt1;
-    else return lds_vt2;
-  };
   auto swz_k = [](int r) { return (r * kChunks / 16) % kChunks; };
-  auto swz_v = [](int r) { return (r / 2) % kChunks; };
+  auto swz_v = [](int r) { return 4 * ((r * kChunks / 16) % (kChunks / 4)); };
 
   // Work item: (pair = seq * H + head, query tile); pairs are dealt to XCDs
   // round robin by pair, the query tiles of a pair go to the same XCD, last
@@ -265,32 +318,38 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
     }
   };
 
-  // Raw V stage vr -> V^T stage vt (fp16, dimension-major, keys paired).
-  auto transpose_v = [&](const char* vr, char* vt) {
+  // bf16 pools: the V chunks this wave's DMA brought into stage dv, to fp16
+  // in place (each lane converts the 16 bytes it loaded).  Called once the
+  // wave's DMA of that tile has landed, before the barrier that publishes it.
+  // (Inline assembly for the same reason as the transposing reads: the
+  // compiler would drain the next tile's DMA before reading this stage.)
+  auto own_v_to_f16 = [&](char* dv) {
+    if constexpr (KV == PA_BF16) {
+      const uint32_t a0 =
+          uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dv)) +
+          wave * kLoadsPerWave * 1024 + lane * 16;
+      u32x4_t w[kLoadsPerWave];
+      lds_read_b128_x<kLoadsPerWave>(a0, w);
 #pragma unroll
-    for (int w0 = 0; w0 < (kBN / 2) * kChunks; w0 += kWaves * 64) {
-      const int w = w0 + tid;
-      if (w < (kBN / 2) * kChunks) {
-        const int kp = w % (kBN / 2);
-        const int dc = w / (kBN / 2);
-        const int r0 = 2 * kp, r1 = 2 * kp + 1;
-        const uint4 x = *(const uint4*)(vr + r0 * kRowBytes + (dc ^ swz_v(r0)) * 16);
-        const uint4 y = *(const uint4*)(vr + r1 * kRowBytes + (dc ^ swz_v(r1)) * 16);
-        const uint32_t a0[4] = {x.x, x.y, x.z, x.w};
-        const uint32_t a1[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // a0[j]: key 2kp, dims 2j and 2j+1; a1[j]: key 2kp+1.  Regroup by
-          // dimension (keys 2kp, 2kp+1 side by side), then convert to fp16.
-          const uint32_t lo = to_f16x2<KV>(interleave_lo(a0[j], a1[j]));  // dim 2j
-          const uint32_t hi = to_f16x2<KV>(interleave_hi(a0[j], a1[j]));  // dim 2j+1
-          const int d = dc * 8 + 2 * j;
-          *(uint32_t*)(vt + d * kVtStride + kp * 4) = lo;
-          *(uint32_t*)(vt + (d + 1) * kVtStride + kp * 4) = hi;
-        }
-      }
+      for (int i = 0; i < kLoadsPerWave; ++i) w[i] = bf16x8_to_f16x8(w[i]);
+      lds_write_b128_x<kLoadsPerWave>(a0, w);
     }
   };
+
+  // Lane offsets of the transposing V reads: for k-step tt and half p of
+  // the A operand's 8 keys, lane l reads dimensions d0 + 4 (j % 4) .. + 4 of
+  // tile row 16 tt + 8 p + rl, with rl = 4 (l / 32) + j / 4, j = l % 16,
+  // d0 = 32 db + 16 ((l / 16) % 2); it then holds keys 16 tt + 8 p + 4 (l / 32)
+  // + 0..3 of dimension 32 db + l % 32 -- the order of P's registers.  The
+  // row's swizzle depends on rl only, so each offset is a lane constant plus
+  // a compile-time part.
+  const int vt_rl = 4 * half + (lane % 16) / 4;
+  const int vt_cl = 2 * ((lane / 16) % 2) + (lane % 4) / 2;   // chunk within the group of 4
+  const int vt_lane = vt_rl * kRowBytes + 16 * vt_cl + 8 * (lane % 2);
+  const int vt_sq = swz_v(vt_rl) / 4;
+  int vt_db[kDBlocks];
+#pragma unroll
+  for (int db = 0; db < kDBlocks; ++db) vt_db[db] = vt_lane + 64 * (db ^ vt_sq);
 
   f32x16_t o[kDBlocks];
 #pragma unroll
@@ -308,13 +367,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
   dma_tile(0, stage_k(S0{}), stage_v(S0{}));
   dma_tile(min(1, n_tiles - 1), stage_k(S1{}), stage_v(S1{}));
   __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile 0 landed
-  __builtin_amdgcn_s_barrier();
-  transpose_v(stage_v(S0{}), stage_vt(S0{}));
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
+  own_v_to_f16(stage_v(S0{}));
+  wg_barrier();
 
-  // One tile: issue tile t+2 (stage st+2), consume tile t (stage st), then
-  // build tile t+1's V^T (stage st+1) once tile t+1 has landed.  Every
+  // One tile: issue tile t+2 (stage st+2), consume tile t (stage st), wait
+  // for this wave's part of tile t+1 and meet the other waves (after which
+  // all of tile t+1 is in LDS and nobody reads stage st any more).  Every
   // iteration issues exactly one tile's DMA, so the waits are exact.
   auto iter = [&](auto st, int t) {
     constexpr int s0 = decltype(st)::value;
@@ -335,7 +393,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
     dma_tile(min(t + 2, n_tiles - 1), stage_k(Snn{}), stage_v(Snn{}));
     __builtin_amdgcn_sched_barrier(0);
     if (active) {
-      const char* vl = stage_vt(st);
+      const char* vl = stage_v(st);
       // S^T = K Q^T : rows = keys of the tile, columns = this wave's queries.
       f32x16_t s;
 #pragma unroll
@@ -394,23 +452,33 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a, int
                             pack_f16(x[8 * tt + 2], x[8 * tt + 3]),
                             pack_f16(x[8 * tt + 4], x[8 * tt + 5]),
                             pack_f16(x[8 * tt + 6], x[8 * tt + 7]));
-      // O^T += V^T P^T : A = V^T rows (dims) with the same key order.
+      // O^T += V^T P^T : A = V^T from the V rows by transposing reads, in
+      // the same key order as P; two dimension blocks' operands per wait.
+      const uint32_t vbase =
+          uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)vl));
+      auto pv_step = [&](auto tt_c) {
+        constexpr int tt = decltype(tt_c)::value;
 #pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) {
-        const char* vrow = vl + (db * 32 + col) * kVtStride;
+        for (int db0 = 0; db0 < kDBlocks; db0 += 2) {
+          uint2 v[4];
+          v[0] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + vt_db[db0]);
+          v[1] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + vt_db[db0]);
+          v[2] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + vt_db[db0 + 1]);
+          v[3] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + vt_db[db0 + 1]);
+          lds_wait_tr(v);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const uint2 lo = *(const uint2*)(vrow + (16 * tt + 4 * half) * 2);
-          const uint2 hi = *(const uint2*)(vrow + (16 * tt + 8 + 4 * half) * 2);
-          o[db] = mfma_pv(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[tt], o[db]);
+          for (int k = 0; k < 2; ++k) {
+            const uint4 va = make_uint4(v[2 * k].x, v[2 * k].y, v[2 * k + 1].x, v[2 * k + 1].y);
+            o[db0 + k] = mfma_pv(va, pf[tt], o[db0 + k]);
+          }
         }
-      }
+      };
+      pv_step(std::integral_constant<int, 0>{});
+      pv_step(std::integral_constant<int, 1>{});
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile t+1 landed
-    __builtin_amdgcn_s_barrier();
-    if (t + 1 < n_tiles) transpose_v(stage_v(Sn{}), stage_vt(Sn{}));
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
+    if (t + 1 < n_tiles) own_v_to_f16(stage_v(Sn{}));
+    wg_barrier();
   };
   // The first iteration is peeled so that both edges into the loop come
   // from the same stage (the same DMA in flight): the compiler's view of
