@@ -29,7 +29,7 @@
 //    stream non-temporal beats both, and shared blocks want both cached);
 //  * the next block's K and V loads are issued before the current block is
 //    consumed (two register buffers), unconditionally: past the wave's last
-//    block they re-read that block (an L2 hit), so the number of loads in
+//    block they re-read its K tile (an L2 hit), so the number of loads in
 //    flight is the same on every path and the compiler's waits keep exactly
 //    one block outstanding while the current one is consumed;
 //  * at the end the groups, then the waves, merge their (max, sum, acc)
@@ -240,10 +240,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   uint4 k0[G::kLoads], v0[G::kLoads], k1[G::kLoads], v1[G::kLoads];
   int p0 = 0, p1 = 0;
 
-  auto issue = [&](uint4* kr, uint4* vr, int& phys, int i) {
-    phys = __builtin_amdgcn_readlane(tab, i);
+  // Loads of the wave's j-th block.  Past its last block (the pipeline's
+  // prefetch after the final one, never consumed) both K and V re-read the
+  // last block's K tile: K loads are ordinary ones, so that tile is still in
+  // the L2, whereas a streamed V tile would come from HBM again.
+  auto issue = [&](uint4* kr, uint4* vr, int& phys, int j) {
+    const bool past = j >= n_w;
+    phys = __builtin_amdgcn_readlane(tab, past ? n_w - 1 : j);
     const char* kp = kbase + int64_t(phys) * blk_stride;
-    const char* vp = vbase + int64_t(phys) * blk_stride;
+    const char* vp = past ? kp : vbase + int64_t(phys) * blk_stride;
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       if (row_ok) {
@@ -304,15 +309,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     m = mx;
   };
 
-  // Two-deep software pipeline over this wave's n_w blocks; the prefetch
-  // past the last one re-reads the last one.
+  // Two-deep software pipeline over this wave's n_w blocks (the prefetch
+  // after the last one is a dummy, see issue()).
   if (n_w > 0) {
     issue(k0, v0, p0, 0);
     for (int i = 0;;) {
-      issue(k1, v1, p1, min(i + 1, n_w - 1));
+      issue(k1, v1, p1, i + 1);
       consume(k0, v0, p0, wave + i * NW);
       if (++i >= n_w) break;
-      issue(k0, v0, p0, min(i + 1, n_w - 1));
+      issue(k0, v0, p0, i + 1);
       consume(k1, v1, p1, wave + i * NW);
       if (++i >= n_w) break;
     }
