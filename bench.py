@@ -255,6 +255,74 @@ class DecodeBench:
                 self.ev.append(tm)
         if timed:
             self.step_bytes.append(self.decode_bytes(lens))
+        self.last = (d, lens)
+
+    def unique_bytes(self, lens):
+        """Bytes of the distinct K/V rows a launch reads: for the shared-prefix
+        workload the prefix once plus every sequence's own tokens; otherwise
+        every row (nothing is shared)."""
+        row = self.H * self.D * ELEM[self.kv]
+        if self.name != "prefix_cow":
+            return self.decode_bytes(lens)
+        prefix = self.cfg["prefix"]
+        return 2 * row * (prefix + int(np.sum(lens - prefix)))
+
+    def cold_series(self, reps=10, flush_mib=512):
+        """pa_decode on the middle layer with the caches cold: a read of
+        flush_mib MiB (twice the 256 MB Infinity Cache) before each timed
+        call, outside the event pair.  A read, not a write: a written flush
+        buffer stays dirty in the Infinity Cache and the decode would then pay
+        for writing it back."""
+        d, lens = self.last
+        pool = self.pools[len(self.pools) // 2]
+        scratch = torch.ones((flush_mib << 20) // 4, dtype=torch.float32, device=self.device)
+        for _ in range(2):
+            scratch.sum()                 # its own dirty lines written back
+        torch.cuda.synchronize()
+        ts = []
+        for r in range(reps):
+            scratch.sum()
+            tm = Timer()
+            tm.start()
+            pa.pa_decode(self.out, self.q[0], pool, d["tables"], d["lens"], self.scale, self.pb,
+                         self.ws)
+            tm.stop()
+            torch.cuda.synchronize()
+            ts.append(tm.seconds())
+        del scratch
+        t = float(np.median(ts))
+        return {"kernel_us": t * 1e6, "logical_GBps": self.decode_bytes(lens) / t / 1e9,
+                "unique_GBps": self.unique_bytes(lens) / t / 1e9,
+                "flush": f"{flush_mib} MiB device read before each of {reps} calls"}
+
+    def cow_copy_us(self, reps=10):
+        """One copy-on-write block copy as the allocator issues it: fork a
+        sequence whose last block is partly filled, append one token (one
+        (src, dst) pair), time pa_copy_blocks of that pair, free the fork."""
+        partial = np.nonzero(self.lens_now() % self.bs != 0)[0]
+        if len(partial) == 0:
+            return None
+        src = int(self.ids[partial[0]])
+        ts = []
+        for r in range(reps):
+            child = 1_000_000 + r
+            self.alloc.fork(src, child)
+            _, pair = self.alloc.append_tokens(child, 1)
+            assert pair is not None
+            pairs = torch.tensor([pair], dtype=torch.int32, device=self.device)
+            tm = Timer()
+            tm.start()
+            pa.pa_copy_blocks(self.pools[0], pairs)
+            tm.stop()
+            torch.cuda.synchronize()
+            ts.append(tm.seconds())
+            self.alloc.free_seq(child)
+        tile = self.H * self.bs * self.D * ELEM[self.kv]
+        t = float(np.median(ts))
+        return {"us": t * 1e6, "bytes": 2 * 2 * tile, "GBps": 2 * 2 * tile / t / 1e9}
+
+    def lens_now(self):
+        return np.array([self.alloc.seq_len(int(i)) for i in self.ids], dtype=np.int64)
 
     def decode_bytes(self, lens):
         """Algorithmic bytes of one pa_decode launch: every cached K and V row
@@ -389,6 +457,12 @@ class PrefillBench:
         t = float(np.mean([tm.seconds() for tm in self.ev]))
         return t, self.flops()
 
+    def hbm_bytes(self):
+        """Algorithmic bytes of one launch: every context and chunk K/V row
+        once, q and out."""
+        row = self.H * self.D * 2
+        return 2 * row * sum(c + self.S for c in self.ctx) + 2 * row * self.B * self.S
+
     def workload_config(self):
         c = self.cfg
         return {"workload": self.name, "batch": self.B, "chunk": self.S, "num_heads": self.H,
@@ -500,6 +574,9 @@ def main():
                            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
                            "traffic": measured_traffic(args.workload, "prefill_kernel"),
                            "kernel": "prefill_kernel", "kernel_us": kt * 1e6}
+        hb = b.hbm_bytes()
+        res["hbm"] = {"bytes_per_launch": hb, "GBps": hb / kt / 1e9,
+                      "frac": hb / kt / 1e9 / HBM_PEAK_GBS}
     else:
         kv_bytes = work                   # per launch (one layer)
         step_s = wall / args.steps
@@ -515,6 +592,13 @@ def main():
         res["hbm_frac_step"] = kv_bytes * b.layers / step_s / 1e9 / HBM_PEAK_GBS
         res["decode_tokens_per_s"] = b.B / step_s
         res["pa_decode_us_per_layer"] = kt * 1e6
+        log("bench: cold-cache series")
+        res["cold"] = b.cold_series()
+        if args.workload == "prefix_cow":
+            ub = b.unique_bytes(b.last[1])
+            res["unique_bytes_per_launch"] = ub
+            res["unique_GBps"] = ub / kt / 1e9
+            res["cow_copy"] = b.cow_copy_us()
     if not args.no_cpu_baseline:
         log("bench: cpu baseline")
         res["cpu_baseline"] = b.cpu_baseline()
