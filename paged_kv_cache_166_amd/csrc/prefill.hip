@@ -140,6 +140,15 @@ constexpr float kRescaleSlack = 8.0f;
 // vmcnt[5:4] << 14).
 constexpr int wait_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
 
+// (v[l mod 32], v[l mod 32 + 32]) in lane l: this lane's value and its
+// partner's in the other half-wave, by gfx950's v_permlane32_swap (a VALU
+// exchange, no LDS round trip).
+__device__ __forceinline__ float2 half_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 typedef __attribute__((address_space(3))) void lds_t;
 
 // s_waitcnt immediate: all LDS / scalar-memory operations done, vector
@@ -166,9 +175,12 @@ __device__ __forceinline__ void load_lds16(const void* src, char* dst) {
 
 // At least three waves per SIMD (at most 168 VGPRs; 48 KiB of LDS fit three
 // workgroups per CU): the loop is latency-bound, and a third workgroup per
-// CU hides more of it than the registers the compiler gives up cost.
+// CU hides more of it than the registers the compiler gives up cost.  (fp16
+// with 4-token blocks, whose tile loads span two blocks, would spill at that
+// bound and keeps two.)
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(KV == PA_F16 && D == 128 && BS == 4 ? 2 : 3)))
 void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   constexpr int kRowBytes = D * 2;
   constexpr int kChunks = D / 8;                       // 16-byte chunks per row
@@ -421,7 +433,14 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       float mx = x[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      // (fp16 pools: the exchange through LDS; the VALU one needs two more
+      // registers there and made the compiler spill inside the loop.)
+      if constexpr (KV == PA_BF16) {
+        const float2 mp = half_pair(mx);
+        mx = fmaxf(mp.x, mp.y) * c;
+      } else {
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      }
       // Rows whose maximum grew past the slack move their reference maximum.
       // The branch is taken for the whole wave (a vote), so the accumulators
       // are touched only on the rare tiles where some row needs it.
@@ -495,7 +514,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // Normalise and store: lane holds query my_row, dims 8*(v/4) + 4*half + v%4.
-  l += __shfl_xor(l, 32);
+  const float2 lp = half_pair(l);
+  l = lp.x + lp.y;
   if (my_row < S && wq0 < S) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t ob = (int64_t(qs + my_row) * H + head) * D;
