@@ -115,3 +115,63 @@ def gather_scales(scales, table, length, block_size):
     if not rows:
         return np.zeros((0, scales.shape[1]), dtype=np.float64)
     return np.asarray(rows, dtype=np.float64)
+
+
+def write_runs(slots, block_size):
+    """Split a call's tokens into runs: maximal groups of consecutive tokens
+    whose slots are consecutive positions of one block.  Returns a list of
+    (block, first position, [token indices])."""
+    slots = np.asarray(slots, dtype=np.int64)
+    runs = []
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        blk, pos = int(s // block_size), int(s % block_size)
+        if runs and runs[-1][0] == blk and slots[runs[-1][2][-1]] == s - 1 and runs[-1][2][-1] == t - 1:
+            runs[-1][2].append(t)
+        else:
+            runs.append((blk, pos, [t]))
+    return runs
+
+
+def write_rows_fp8_upkeep(cache_codes, x_f32, slots, scales, block_size):
+    """fp8 store that keeps each (block, head) scale at amax / 448 of the rows
+    the block holds (reading of the blog article's mixed-precision KV, section
+    2.3, for blocks that fill a few tokens at a time).
+
+    For each run of the call (one block, consecutive positions p0 ..), and
+    each head, in float32:
+      s_run = amax(|x| over the run's rows) / 448;
+      s_old = 0 if the run starts the block (p0 == 0) else scales[block, head];
+      s_new = max(s_old, s_run);
+      if s_new > s_old and p0 > 0, the block's earlier rows 0 .. p0-1 are
+      requantised: code' = RNE-saturate((decode(code) * s_old) / s_new);
+      the run's rows are stored as RNE-saturate(x / s_new);
+      scales[block, head] = s_new.
+    While a block's scale is 0 (every value so far zero) the divisor is 1, so
+    zeros keep their sign.  Each block's new rows must form one run of the
+    call, at positions after the rows it already holds (what the allocator's
+    slot mappings give).  cache_codes [N, H, bs, D] uint8, x_f32 [T, H, D],
+    scales [N, H] float32, all updated in place.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    f448 = np.float32(fp8.MAX_FINITE)
+    runs = write_runs(slots, block_size)
+    blocks = [r[0] for r in runs]
+    if len(set(blocks)) != len(blocks):
+        raise ValueError("a block's new rows must form one run of the call")
+    for blk, p0, toks in runs:
+        rows = x[toks]                                     # [n, H, D]
+        n = len(toks)
+        for h in range(cache_codes.shape[1]):
+            s_run = np.float32(np.abs(rows[:, h, :]).max()) / f448
+            s_old = np.float32(0.0) if p0 == 0 else np.float32(scales[blk, h])
+            s_new = max(s_old, s_run)
+            div_new = s_new if s_new > 0 else np.float32(1.0)
+            if p0 > 0 and s_new > s_old:
+                old = cache_codes[blk, h, :p0, :]
+                v = fp8.decode(old).astype(np.float32) * s_old   # float32 product
+                cache_codes[blk, h, :p0, :] = fp8.quantize_f32(v, div_new)
+            cache_codes[blk, h, p0:p0 + n, :] = fp8.quantize_f32(rows[:, h, :], div_new)
+            scales[blk, h] = s_new
+    return cache_codes
