@@ -170,6 +170,8 @@ class DecodeBench:
         # the pools' stream flag: only when no block is shared by two sequences
         # (every workload but the shared-prefix one)
         self.stream_kv = (workload != "prefix_cow") if stream_kv is None else stream_kv
+        # fp8: the step's appended tokens keep each block's scale at its amax / 448
+        self.auto_scale = self.kv == "fp8"
         self.lens0 = lens0
         self.alloc = pa.Allocator(self.N, self.bs, W.free_order(cfg["seed"], self.N))
         g = torch.Generator(device=device)
@@ -209,7 +211,7 @@ class DecodeBench:
 
     def _filled_pool(self, g):
         pool = pa.PagedPool.empty(self.N, self.H, self.bs, self.D, self.kv, self.device,
-                                  stream_kv=self.stream_kv)
+                                  stream_kv=self.stream_kv, fp8_auto_scale=self.auto_scale)
         for t in (pool.k_cache, pool.v_cache):
             for i in range(0, self.N, 1024):
                 n = min(1024, self.N - i)
@@ -266,6 +268,37 @@ class DecodeBench:
             return self.decode_bytes(lens)
         prefix = self.cfg["prefix"]
         return 2 * row * (prefix + int(np.sum(lens - prefix)))
+
+    def fp8_write_series(self, tokens=4096, reps=20):
+        """A prefill-sized fp8 write: `tokens` bf16 rows of K and V into fresh
+        blocks of a separate pool, with scale upkeep and with caller-set
+        scales (the plain write), event-timed; algorithmic bytes = the input
+        rows read once + the codes and scales written."""
+        H, D, bs = self.H, self.D, self.bs
+        nb = -(-tokens // bs)
+        res = {"tokens": tokens}
+        g = torch.Generator(device=self.device)
+        g.manual_seed(1)
+        k = torch.randn((tokens, H, D), generator=g, device=self.device).to(torch.bfloat16)
+        v = torch.randn((tokens, H, D), generator=g, device=self.device).to(torch.bfloat16)
+        slots = torch.arange(tokens, dtype=torch.int64, device=self.device)
+        nbytes = 2 * tokens * H * D * (2 + 1) + 2 * nb * H * 4
+        for name, auto in (("upkeep", True), ("plain", False)):
+            pool = pa.PagedPool.empty(nb, H, bs, D, "fp8", self.device, fp8_auto_scale=auto)
+            ts = []
+            for r in range(reps + 3):
+                tm = Timer()
+                tm.start()
+                pa.pa_reshape_and_cache(pool, k, v, slots)
+                tm.stop()
+                torch.cuda.synchronize()
+                if r >= 3:
+                    ts.append(tm.seconds())
+            t = float(np.median(ts))
+            res[name] = {"us": t * 1e6, "GBps": nbytes / t / 1e9}
+            del pool
+        res["bytes"] = nbytes
+        return res
 
     def cold_series(self, reps=10, flush_mib=512):
         """pa_decode on the middle layer with the caches cold: a read of
@@ -352,6 +385,7 @@ class DecodeBench:
         d["partition_blocks"] = self.pb or pa.pa_decode_auto_partition_blocks(self.pool, self.B,
                                                                               self.maxb)
         d["stream_kv"] = self.stream_kv
+        d["fp8_auto_scale"] = self.auto_scale
         return d
 
     def cpu_baseline(self, budget_s=10.0):
@@ -594,6 +628,8 @@ def main():
         res["pa_decode_us_per_layer"] = kt * 1e6
         log("bench: cold-cache series")
         res["cold"] = b.cold_series()
+        if args.workload == "long_fp8_decode":
+            res["fp8_write"] = b.fp8_write_series()
         if args.workload == "prefix_cow":
             ub = b.unique_bytes(b.last[1])
             res["unique_bytes_per_launch"] = ub

@@ -84,6 +84,25 @@ typedef struct pa_pool {
  */
 #define PA_POOL_STREAM_KV 1
 
+/*
+ * PA_POOL_FP8_AUTO_SCALE (fp8 pools only): pa_reshape_and_cache keeps each
+ *   (block, head) scale at amax / 448 of the rows the block holds (the blog
+ *   article's mixed-precision KV, section 2.3, for blocks that fill a few
+ *   tokens at a time), for K and V separately.  The call's tokens are taken
+ *   in runs: consecutive tokens whose slots are consecutive positions of one
+ *   block.  For each run and head, in float32: s_run = amax(|rows|) / 448;
+ *   s_old = 0 if the run starts the block (position 0), else the block's
+ *   scale; s_new = max(s_old, s_run).  If s_new > s_old, the block's earlier
+ *   rows are requantised, code = RNE-saturate((decode(code) * s_old) /
+ *   s_new); the run's rows are stored as RNE-saturate(x / s_new); the scale
+ *   becomes s_new.  While a scale is 0 (all values so far zero) the divisor
+ *   is 1.  Precondition (what the allocator's slot mappings give): each
+ *   block's new rows form one run of the call, after the rows the block
+ *   already holds.  Without the flag the caller owns the scales and rows are
+ *   stored with the block's existing scale.
+ */
+#define PA_POOL_FP8_AUTO_SCALE 2
+
 /* ---------------------------------------------------------------- GPU calls */
 
 /*
@@ -96,7 +115,9 @@ typedef struct pa_pool {
  *                 kv_dtype and the rows are copied bit for bit.  For fp8 pools
  *                 in_dtype is f32, f16 or bf16 and each element is stored as
  *                 RNE-saturate(x / scale[block][head]) with the division in
- *                 float32; the block's scale must already be set.
+ *                 float32; the block's scale must already be set, unless the
+ *                 pool has PA_POOL_FP8_AUTO_SCALE (then the call maintains
+ *                 the scales, see that flag).
  *   slot_mapping  device, [num_tokens] int64; a negative slot skips the row.
  * Two rows of one call must not name the same slot.
  */

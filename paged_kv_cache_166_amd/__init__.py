@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_SEQ = 0, -1, -2, -3, -4, -5
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_POOL_STREAM_KV = 1
+PA_POOL_FP8_AUTO_SCALE = 2
 
 _DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
           torch.float8_e4m3fn: PA_FP8_E4M3}
@@ -138,7 +139,7 @@ class PagedPool:
     """
 
     def __init__(self, k_cache, v_cache, k_scale=None, v_scale=None, kv_dtype=None,
-                 stream_kv=False):
+                 stream_kv=False, fp8_auto_scale=False):
         assert k_cache.shape == v_cache.shape and k_cache.dim() == 4
         assert k_cache.is_contiguous() and v_cache.is_contiguous()
         self.k_cache, self.v_cache = k_cache, v_cache
@@ -151,7 +152,9 @@ class PagedPool:
         self._struct = _Pool(k_cache.data_ptr(), v_cache.data_ptr(),
                              k_scale.data_ptr() if k_scale is not None else 0,
                              v_scale.data_ptr() if v_scale is not None else 0,
-                             N, H, bs, D, kv_dtype, PA_POOL_STREAM_KV if stream_kv else 0)
+                             N, H, bs, D, kv_dtype,
+                             (PA_POOL_STREAM_KV if stream_kv else 0)
+                             | (PA_POOL_FP8_AUTO_SCALE if fp8_auto_scale else 0))
 
     @property
     def stream_kv(self):
@@ -164,6 +167,17 @@ class PagedPool:
         self._struct.flags = (self._struct.flags & ~PA_POOL_STREAM_KV) | (PA_POOL_STREAM_KV if on else 0)
 
     @property
+    def fp8_auto_scale(self):
+        """True: pa_reshape_and_cache keeps each (block, head) scale at the
+        amax of the block's rows / 448 (PA_POOL_FP8_AUTO_SCALE)."""
+        return bool(self._struct.flags & PA_POOL_FP8_AUTO_SCALE)
+
+    @fp8_auto_scale.setter
+    def fp8_auto_scale(self, on):
+        f = self._struct.flags & ~PA_POOL_FP8_AUTO_SCALE
+        self._struct.flags = f | (PA_POOL_FP8_AUTO_SCALE if on else 0)
+
+    @property
     def device(self):
         return self.k_cache.device
 
@@ -172,7 +186,7 @@ class PagedPool:
 
     @staticmethod
     def empty(num_blocks, num_heads, block_size, head_dim, kv_dtype, device, fill=None,
-              stream_kv=False):
+              stream_kv=False, fp8_auto_scale=False):
         """Allocate a pool (and fp8 scales of 1.0)."""
         tdt = torch.uint8 if kv_dtype == "fp8" else TORCH_DTYPE[kv_dtype]
         shape = (num_blocks, num_heads, block_size, head_dim)
@@ -185,7 +199,8 @@ class PagedPool:
         if kv_dtype == "fp8":
             ks = torch.ones((num_blocks, num_heads), dtype=torch.float32, device=device)
             vs = torch.ones((num_blocks, num_heads), dtype=torch.float32, device=device)
-        return PagedPool(k, v, ks, vs, _NAME[kv_dtype], stream_kv=stream_kv)
+        return PagedPool(k, v, ks, vs, _NAME[kv_dtype], stream_kv=stream_kv,
+                         fp8_auto_scale=fp8_auto_scale)
 
 
 # ---------------------------------------------------------------- GPU calls

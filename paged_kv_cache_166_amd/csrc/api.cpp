@@ -29,7 +29,10 @@ pa_status check_pool(const char* fn, const pa_pool* p) {
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", fn, p->head_dim);
   if (!valid_dtype(p->kv_dtype)) return fail(PA_ERR_INVALID, "%s: kv_dtype %d", fn, p->kv_dtype);
-  if (p->flags & ~PA_POOL_STREAM_KV) return fail(PA_ERR_INVALID, "%s: unknown pool flags 0x%x", fn, p->flags);
+  if (p->flags & ~(PA_POOL_STREAM_KV | PA_POOL_FP8_AUTO_SCALE))
+    return fail(PA_ERR_INVALID, "%s: unknown pool flags 0x%x", fn, p->flags);
+  if ((p->flags & PA_POOL_FP8_AUTO_SCALE) && p->kv_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_INVALID, "%s: PA_POOL_FP8_AUTO_SCALE on a pool that is not fp8", fn);
   if (p->kv_dtype == PA_FP8_E4M3) {
     if (!p->k_scale || !p->v_scale) return fail(PA_ERR_INVALID, "%s: fp8 pool without scales", fn);
   }
@@ -90,7 +93,7 @@ pa_status pa_reshape_and_cache(const pa_pool* pool, const void* key, const void*
   pa::CacheWriteArgs a{pool->k_cache, pool->v_cache, pool->k_scale, pool->v_scale,
                        key,           value,         slot_mapping,  num_tokens,
                        pool->num_heads, pool->block_size, pool->head_dim, in_dtype,
-                       pool->kv_dtype};
+                       pool->kv_dtype,  (pool->flags & PA_POOL_FP8_AUTO_SCALE) != 0};
   return hip_status(fn, pa::launch_reshape_and_cache(a, stream));
 }
 

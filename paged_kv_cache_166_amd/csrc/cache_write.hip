@@ -6,7 +6,8 @@
 // moves 8 elements of one (token, head) row; a row of 128 elements is 16
 // threads, so each wave writes 4 whole rows with contiguous 16-byte (or
 // 8-byte for fp8) stores.  fp8 pools store RNE-saturate(x / scale) with the
-// block's existing per-head scale (the blog article's mixed-precision KV).
+// block's existing per-head scale (the blog article's mixed-precision KV), or,
+// with scale upkeep, keep each block's scale at the amax of its rows / 448.
 //
 // copy_blocks copies whole (block, head) tiles of K and V, and the fp8
 // scales, for the copy-on-write step (DataWhale notes section 4).
@@ -89,6 +90,118 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
   *(uint2*)((uint8_t*)a.v_cache + dst_e) = make_uint2(pack4_fp8(y), pack4_fp8(y + 4));
 }
 
+// Eight codes requantised from scale s_old to divisor d:
+// RNE-saturate((decode(code) * s_old) / d), both steps rounded in float32.
+__device__ __forceinline__ uint2 requant8(uint2 w, float s_old, float d) {
+  float y[8];
+  const float2_t a0 = fp8x2_lo(w.x), a1 = fp8x2_hi(w.x), b0 = fp8x2_lo(w.y), b1 = fp8x2_hi(w.y);
+  const float x[8] = {a0.x, a0.y, a1.x, a1.y, b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fp8_prep(__fmul_rn(x[i], s_old), d);
+  return make_uint2(pack4_fp8(y), pack4_fp8(y + 4));
+}
+
+// Largest value over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// fp8 write with scale upkeep (PA_POOL_FP8_AUTO_SCALE).  Grid (window of
+// tokens, head), one wave each.  The call's tokens form runs: consecutive
+// tokens writing consecutive positions of one block.  The wave whose window
+// holds a run's first token does the whole run for its head: amax of the run's rows, new scale
+// max(old, amax / 448) (old = 0 when the run starts the block), the block's
+// earlier rows requantised if the scale grew, the run's rows stored, the
+// scale written -- K, then V (a window's runs one after another).  Runs of
+// different blocks touch disjoint tiles and scales, so no wave waits for
+// another.  Every step issues all its loads at once (a run is at most 32
+// rows of at most 128 elements: at most 8 chunks of 8 per lane), so a run
+// costs a few memory round trips, not one per row.
+constexpr int kMaxChunksPerLane = 8;   // 32 rows x 128 / 8 elements / 64 lanes
+
+__device__ __forceinline__ void upkeep_one(const CacheWriteArgs& a, const void* in, uint8_t* tile,
+                                           float* scale, int64_t t, int h, int p0, int n,
+                                           int lane) {
+  const int D = a.head_dim;
+  const int chunks = D / 8;
+  const int in_b = dtype_bytes(a.in_dtype);
+  const int H = a.num_heads;
+  const int total = n * chunks;
+  float x[kMaxChunksPerLane][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxChunksPerLane; ++k) {
+    const int i = lane + 64 * k;
+    if (i < total) {
+      const int r = i / chunks, c = i % chunks;
+      load8_f32((const char*)in + (((t + r) * H + h) * D + c * 8) * in_b, a.in_dtype, x[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[k][e]));
+    }
+  }
+  amax = wave_max(amax);
+  const float s_old = p0 == 0 ? 0.f : *scale;
+  const float s_new = fmaxf(s_old, __fdiv_rn(amax, 448.f));
+  const float d = s_new > 0.f ? s_new : 1.f;
+  if (p0 > 0 && s_new > s_old) {
+    uint2 w[kMaxChunksPerLane];
+#pragma unroll
+    for (int k = 0; k < kMaxChunksPerLane; ++k) {
+      const int i = lane + 64 * k;
+      if (i < p0 * chunks) w[k] = *(const uint2*)(tile + i * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxChunksPerLane; ++k) {
+      const int i = lane + 64 * k;
+      if (i < p0 * chunks) *(uint2*)(tile + i * 8) = requant8(w[k], s_old, d);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxChunksPerLane; ++k) {
+    const int i = lane + 64 * k;
+    if (i < total) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = fp8_prep(x[k][e], d);
+      *(uint2*)(tile + p0 * D + i * 8) = make_uint2(pack4_fp8(y), pack4_fp8(y + 4));
+    }
+  }
+  if (lane == 0) *scale = s_new;
+}
+
+__global__ __launch_bounds__(64) void reshape_fp8_upkeep_kernel(CacheWriteArgs a, int window) {
+  const int64_t t0 = int64_t(blockIdx.x) * window;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int bs = a.block_size;
+  // Run heads among this wave's tokens t0 .. t0 + window - 1 (window <= 64):
+  // a token with a slot whose previous token did not write the previous
+  // position of the same block.
+  const int64_t tl = t0 + lane;
+  bool head = false;
+  if (lane < window && tl < a.num_tokens) {
+    const int64_t s = a.slots[tl];
+    head = s >= 0 && !(tl > 0 && s % bs > 0 && a.slots[tl - 1] == s - 1);
+  }
+  uint64_t heads = __ballot(head);
+  while (heads) {
+    const int64_t t = t0 + __builtin_ctzll(heads);
+    heads &= heads - 1;
+    const int64_t s = a.slots[t];
+    const int64_t blk = s / bs;
+    const int p0 = int(s % bs);
+    // Run length in one round trip: lane i checks token t + i (i < bs - p0).
+    const bool cont = lane < bs - p0 && t + lane < a.num_tokens && a.slots[t + lane] == s + lane;
+    const int n = int(__builtin_ctzll(~__ballot(cont)));   // leading run of ones
+    const int64_t si = blk * a.num_heads + h;
+    const int64_t tile = si * bs * a.head_dim;
+    upkeep_one(a, a.key, (uint8_t*)a.k_cache + tile, a.k_scale + si, t, h, p0, n, lane);
+    upkeep_one(a, a.value, (uint8_t*)a.v_cache + tile, a.v_scale + si, t, h, p0, n, lane);
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
   const int pair = blockIdx.x;
   const int h = blockIdx.y;
@@ -111,6 +224,17 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream) {
   const int64_t n = int64_t(a.num_tokens) * a.num_heads * (a.head_dim / 8);
   if (n == 0) return hipSuccess;
+  if (a.kv_dtype == PA_FP8_E4M3 && a.scale_upkeep) {
+    // One wave per (window of tokens, head).  Large calls are mostly runs of
+    // a whole block (prefill chunks): a window of one block keeps every wave
+    // busy.  Small calls are mostly one-token runs (decode): one token per
+    // wave runs them all at once.
+    const int window = a.num_tokens > 1024 ? a.block_size : 1;
+    const unsigned waves = unsigned((int64_t(a.num_tokens) + window - 1) / window);
+    hipLaunchKernelGGL(reshape_fp8_upkeep_kernel, dim3(waves, unsigned(a.num_heads)), dim3(64), 0,
+                       stream, a, window);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0,
                      stream, a);
   return hipGetLastError();

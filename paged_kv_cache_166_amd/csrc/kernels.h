@@ -34,8 +34,8 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int bl
 struct CacheWriteArgs {
   void* k_cache;
   void* v_cache;
-  const float* k_scale;
-  const float* v_scale;
+  float* k_scale;     // fp8: read, and with scale_upkeep also written
+  float* v_scale;
   const void* key;
   const void* value;
   const int64_t* slots;
@@ -45,6 +45,7 @@ struct CacheWriteArgs {
   int32_t head_dim;
   int32_t in_dtype;
   int32_t kv_dtype;
+  int32_t scale_upkeep;  // fp8: keep each (block, head) scale at the rows' amax / 448
 };
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);

@@ -57,7 +57,7 @@ class Scenario:
     on the GPU and through the oracle on the host, from the same inputs."""
 
     def __init__(self, num_blocks, num_heads, block_size, head_dim, kv, seed, device="cuda",
-                 in_dtype=None, scale_range=(0.004, 0.02)):
+                 in_dtype=None, scale_range=(0.004, 0.02), fp8_auto_scale=False):
         self.N, self.H, self.bs, self.D, self.kv = num_blocks, num_heads, block_size, head_dim, kv
         self.in_dtype = in_dtype or ("bf16" if kv == "fp8" else kv)
         self.rng = np.random.default_rng(seed)
@@ -65,7 +65,9 @@ class Scenario:
         self.alloc = pa.Allocator(num_blocks, block_size, order)
         self.ora = OracleAllocator(num_blocks, block_size, order)
         self.device = device
-        self.pool = pa.PagedPool.empty(num_blocks, num_heads, block_size, head_dim, kv, device)
+        self.auto_scale = fp8_auto_scale
+        self.pool = pa.PagedPool.empty(num_blocks, num_heads, block_size, head_dim, kv, device,
+                                       fp8_auto_scale=fp8_auto_scale)
         shape = (num_blocks, num_heads, block_size, head_dim)
         self.ok = np.full(shape, SENTINEL[kv], dtype=BITS[kv])
         self.ov = self.ok.copy()
@@ -89,12 +91,14 @@ class Scenario:
                 t.fill_(SENTINEL["fp8"])
 
     # -- writes ---------------------------------------------------------------
-    def _write(self, slots, n):
-        """Draw n rows of K and V, write them at slots on both sides."""
+    def _write(self, slots, n, amp=1.0):
+        """Draw n rows of K and V (N(0, amp^2)), write them at slots on both
+        sides.  amp may be an array broadcast over [n, H, 1]."""
         if n == 0:
             return
-        k32 = self.rng.standard_normal((n, self.H, self.D), dtype=np.float32)
-        v32 = self.rng.standard_normal((n, self.H, self.D), dtype=np.float32)
+        a = np.asarray(amp, dtype=np.float32)
+        k32 = self.rng.standard_normal((n, self.H, self.D), dtype=np.float32) * a
+        v32 = self.rng.standard_normal((n, self.H, self.D), dtype=np.float32) * a
         kb, vb = to_bits(k32, self.in_dtype), to_bits(v32, self.in_dtype)
         kd = bits_to_device(kb, self.in_dtype, self.device)
         vd = bits_to_device(vb, self.in_dtype, self.device)
@@ -103,20 +107,21 @@ class Scenario:
         if self.kv == "fp8":
             kf = values_f64(kb, self.in_dtype).astype(np.float32)
             vf = values_f64(vb, self.in_dtype).astype(np.float32)
-            C.write_rows_fp8(self.ok, kf, slots, self.oks, self.bs)
-            C.write_rows_fp8(self.ov, vf, slots, self.ovs, self.bs)
+            w = C.write_rows_fp8_upkeep if self.auto_scale else C.write_rows_fp8
+            w(self.ok, kf, slots, self.oks, self.bs)
+            w(self.ov, vf, slots, self.ovs, self.bs)
         else:
             C.write_rows(self.ok, kb, slots, self.bs)
             C.write_rows(self.ov, vb, slots, self.bs)
 
-    def prompt(self, seq, n):
+    def prompt(self, seq, n, amp=1.0):
         s_lib = self.alloc.alloc_prompt(seq, n)
         s_ora = self.ora.alloc_prompt(seq, n)
         assert list(s_lib) == s_ora
         self.seqs.append(seq)
-        self._write(s_ora, n)
+        self._write(s_ora, n, amp)
 
-    def append(self, seq, n=1):
+    def append(self, seq, n=1, amp=1.0):
         s_lib, cow_lib = self.alloc.append_tokens(seq, n)
         s_ora, cow_ora = self.ora.append_tokens(seq, n)
         assert list(s_lib) == s_ora and cow_lib == cow_ora
@@ -125,8 +130,20 @@ class Scenario:
             pa.pa_copy_blocks(self.pool, pairs)
             C.copy_blocks(self.ok, [cow_ora], self.oks)
             C.copy_blocks(self.ov, [cow_ora], self.ovs)
-        self._write(s_ora, n)
+        self._write(s_ora, n, amp)
         return cow_ora
+
+    def write_batch(self, seqs, n=1, amp=1.0):
+        """Append n tokens (or n[i] to seqs[i]) and write them in one call (the
+        slot mapping of a batched decode or prefill step)."""
+        slots = []
+        ns = n if isinstance(n, (list, tuple)) else [n] * len(seqs)
+        for sq, k in zip(seqs, ns):
+            s_lib, cow = self.alloc.append_tokens(sq, k)
+            s_ora, cow_o = self.ora.append_tokens(sq, k)
+            assert list(s_lib) == s_ora and cow is None and cow_o is None
+            slots += s_ora
+        self._write(slots, len(slots), amp)
 
     def fork(self, parent, child):
         self.alloc.fork(parent, child)

@@ -51,7 +51,8 @@ def _decode(pool, **kw):
     ("num_blocks", 0, pa.PA_ERR_INVALID),
     ("k_cache", 0x10040, pa.PA_ERR_INVALID),      # not 128-byte aligned
     ("k_cache", 0, pa.PA_ERR_INVALID),
-    ("flags", 2, pa.PA_ERR_INVALID),               # unknown pool flag
+    ("flags", 4, pa.PA_ERR_INVALID),               # unknown pool flag
+    ("flags", pa.PA_POOL_FP8_AUTO_SCALE, pa.PA_ERR_INVALID),   # auto scale on an f16 pool
 ])
 def test_pool_checks(field, value, code):
     assert _decode(_fake_pool(**{field: value})) == code
