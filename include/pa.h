@@ -262,6 +262,58 @@ int32_t pa_block_refcount(const pa_allocator* a, int32_t block);
  * made by copy-on-write, [3] OOM refusals, [4] live sequences. */
 pa_status pa_allocator_stats(const pa_allocator* a, int64_t* out5);
 
+/* ------------------------------------------------------- host prefix index */
+
+/*
+ * A prefix index over token ids bound to one allocator (the DataWhale notes'
+ * RadixAttention section: cached token sequences in a radix tree whose
+ * nodes point at the physical KV blocks; a new prompt reuses the blocks of
+ * its longest cached prefix and only the rest is computed; an edge is split
+ * where a new sequence leaves it).  Token ids are int32.  Not thread-safe;
+ * destroy the index before its allocator.
+ *
+ * Blocks: an inserted sequence is an entry.  It provides the positions from
+ * its divergence point d (its match length before insertion) to its end and
+ * holds one allocator reference on each of its blocks covering one of them
+ * (indices d / bs .. (n-1) / bs), so cached blocks outlive the sequence.
+ * Block j of a hit of h tokens is block j of the earliest entry whose common
+ * prefix with the prompt is longer than min((j+1) * bs, h) - 1.
+ */
+typedef struct pa_prefix_index pa_prefix_index;
+
+pa_status pa_prefix_index_create(pa_allocator* a, pa_prefix_index** out);
+/* Releases the index's references (as pa_prefix_clear), then frees it. */
+void pa_prefix_index_destroy(pa_prefix_index* x);
+
+/* Cache the first num_tokens tokens of live sequence seq_id (which holds at
+ * least that many).  *divergence (may be NULL) receives d.  A sequence that
+ * later writes into a partly filled block the index references copies it
+ * first (copy-on-write). */
+pa_status pa_prefix_insert(pa_prefix_index* x, int64_t seq_id, const int32_t* tokens,
+                           int32_t num_tokens, int32_t* divergence);
+
+/* Longest common prefix of tokens with any cached entry. */
+pa_status pa_prefix_match(const pa_prefix_index* x, const int32_t* tokens, int32_t num_tokens,
+                          int32_t* hit_len);
+
+/* New sequence seq_id for a prompt of num_tokens tokens: the blocks of its
+ * longest cached prefix (h tokens, one reference each), length h, then an
+ * append of the other num_tokens - h tokens: slots_out[0 .. num_tokens-h)
+ * receives their slots, and (*cow_src_dst, *num_cow = 1) the whole-block
+ * copy needed when the hit ends inside a block.  All or nothing: OOM
+ * changes nothing.  A full hit leaves no suffix. */
+pa_status pa_alloc_prompt_cached(pa_prefix_index* x, int64_t seq_id, const int32_t* tokens,
+                                 int32_t num_tokens, int32_t* hit_len, int64_t* slots_out,
+                                 int32_t* cow_src_dst, int32_t* num_cow);
+
+/* Drop every entry: references released entry by entry in insertion order,
+ * each entry's blocks by index (blocks reaching zero go back to the free
+ * list in that order). */
+pa_status pa_prefix_clear(pa_prefix_index* x);
+
+/* [0] entries, [1] tree nodes (root included), [2] block references held. */
+pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out3);
+
 const char* pa_last_error(void);
 
 #ifdef __cplusplus

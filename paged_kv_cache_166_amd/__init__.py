@@ -41,6 +41,8 @@ EXPORTS = [
     "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_prompt", "pa_append_tokens",
     "pa_append_tokens_batch", "pa_fork", "pa_free_seq", "pa_get_block_table",
     "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
+    "pa_prefix_index_create", "pa_prefix_index_destroy", "pa_prefix_insert", "pa_prefix_match",
+    "pa_alloc_prompt_cached", "pa_prefix_clear", "pa_prefix_stats",
     "pa_last_error",
 ]
 
@@ -84,6 +86,13 @@ def _load():
         "pa_num_free_blocks": (I32, [VP]),
         "pa_block_refcount": (I32, [VP, I32]),
         "pa_allocator_stats": (I32, [VP, pi64]),
+        "pa_prefix_index_create": (I32, [VP, ctypes.POINTER(VP)]),
+        "pa_prefix_index_destroy": (None, [VP]),
+        "pa_prefix_insert": (I32, [VP, I64, pi32, I32, pi32]),
+        "pa_prefix_match": (I32, [VP, pi32, I32, pi32]),
+        "pa_alloc_prompt_cached": (I32, [VP, I64, pi32, I32, pi32, pi64, pi32, pi32]),
+        "pa_prefix_clear": (I32, [VP]),
+        "pa_prefix_stats": (I32, [VP, pi64]),
         "pa_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -368,3 +377,62 @@ class Allocator:
         _check(lib.pa_allocator_stats(self._h, _i64p(out)), "pa_allocator_stats")
         return dict(used=int(out[0]), shared=int(out[1]), cow_copies=int(out[2]),
                     oom=int(out[3]), seqs=int(out[4]))
+
+
+class PrefixIndex:
+    """Host prefix index over token ids bound to an Allocator (C++ radix
+    tree): insert cached sequences, match prompts, allocate a prompt that
+    reuses its longest cached prefix.  Keeps the allocator alive."""
+
+    def __init__(self, alloc):
+        import numpy as np
+        self._np = np
+        self.alloc = alloc
+        h = ctypes.c_void_p()
+        _check(lib.pa_prefix_index_create(alloc._h, ctypes.byref(h)), "pa_prefix_index_create")
+        self._h = h
+
+    def __del__(self, _destroy=lib.pa_prefix_index_destroy):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _destroy(h)
+            self._h = None
+
+    def _tok(self, tokens):
+        return self._np.ascontiguousarray(self._np.asarray(tokens, dtype=self._np.int32))
+
+    def insert(self, seq_id, tokens):
+        """Cache the first len(tokens) tokens of seq_id; returns the divergence point."""
+        t = self._tok(tokens)
+        d = self._np.zeros(1, dtype=self._np.int32)
+        _check(lib.pa_prefix_insert(self._h, seq_id, _i32p(t), len(t), _i32p(d)), "pa_prefix_insert")
+        return int(d[0])
+
+    def match(self, tokens):
+        t = self._tok(tokens)
+        h = self._np.zeros(1, dtype=self._np.int32)
+        _check(lib.pa_prefix_match(self._h, _i32p(t), len(t), _i32p(h)), "pa_prefix_match")
+        return int(h[0])
+
+    def alloc_prompt_cached(self, seq_id, tokens):
+        """Returns (hit, slots of the suffix, cow pair or None)."""
+        np = self._np
+        t = self._tok(tokens)
+        hit = np.zeros(1, dtype=np.int32)
+        slots = np.empty(max(len(t), 1), dtype=np.int64)
+        pair = np.empty(2, dtype=np.int32)
+        ncow = np.zeros(1, dtype=np.int32)
+        _check(lib.pa_alloc_prompt_cached(self._h, seq_id, _i32p(t), len(t), _i32p(hit),
+                                          _i64p(slots), _i32p(pair), _i32p(ncow)),
+               "pa_alloc_prompt_cached")
+        h = int(hit[0])
+        return h, slots[:len(t) - h], ((int(pair[0]), int(pair[1])) if ncow[0] else None)
+
+    def clear(self):
+        _check(lib.pa_prefix_clear(self._h), "pa_prefix_clear")
+
+    def stats(self):
+        out = self._np.zeros(3, dtype=self._np.int64)
+        _check(lib.pa_prefix_stats(self._h, _i64p(out)), "pa_prefix_stats")
+        return {"entries": int(out[0]), "nodes": int(out[1]), "referenced_blocks": int(out[2])}
+

@@ -1,0 +1,255 @@
+// Prefix index over token ids behind the pa_prefix_* calls of pa.h.
+//
+// The DataWhale notes' RadixAttention section: cached token sequences kept in
+// a radix (compressed prefix) tree whose edges hold runs of tokens and whose
+// nodes point at the physical KV blocks; a new prompt is matched from the
+// root by longest common prefix, the matched part reuses its blocks and only
+// the unmatched suffix is computed; a node is split where a new sequence
+// leaves the middle of an edge.
+//
+// Blocks: each inserted sequence is an entry with its block table.  An entry
+// provides the positions from its divergence point d (its match length
+// before insertion) to its end, and holds one allocator reference on each of
+// its blocks that covers one of them (indices d / bs .. (n-1) / bs), so
+// cached blocks outlive their sequence.  Every tree node remembers the entry
+// that created its positions (a split keeps it on both halves); block j of a
+// hit of h tokens comes from the creator of the node holding position
+// min((j+1) bs, h) - 1, the last hit position in that block -- an entry whose
+// tokens equal the prompt up to there, so its block j holds the right rows.
+// A hit that ends inside a block shares that partly filled block; the
+// allocator's copy-on-write copies it on the sequence's first write.
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "allocator_impl.h"
+#include "pa.h"
+#include "status.h"
+
+namespace {
+
+struct Node {
+  std::vector<int32_t> edge;  // tokens on the edge into this node
+  int64_t start = 0;          // depth of edge[0]
+  int32_t creator = -1;       // entry whose insertion created these positions
+  int32_t parent = -1;
+  std::unordered_map<int32_t, int32_t> kids;  // first token of a child's edge -> node
+};
+
+struct Entry {
+  std::vector<int32_t> table;  // the sequence's blocks covering its n tokens
+  std::vector<int32_t> refs;   // blocks this entry holds a reference on, by index
+};
+
+// One step of a walk: node, and the depth range [lo, hi) of the prompt it
+// matched along that node's edge.
+struct Seg {
+  int32_t node;
+  int64_t lo, hi;
+};
+
+}  // namespace
+
+struct pa_prefix_index {
+  pa_allocator* alloc = nullptr;
+  std::vector<Node> nodes;  // nodes[0] is the root (empty edge)
+  std::vector<Entry> entries;
+
+  // Longest match of tokens from the root; the segments walked, and where
+  // the walk stopped (node, offset in its edge) for an insertion.
+  int64_t walk(const int32_t* t, int64_t n, std::vector<Seg>* segs, int32_t* stop_node,
+               int64_t* stop_off) const {
+    int32_t cur = 0;
+    int64_t depth = 0;
+    if (stop_node) *stop_node = 0;
+    if (stop_off) *stop_off = 0;
+    while (depth < n) {
+      const Node& c = nodes[cur];
+      auto it = c.kids.find(t[depth]);
+      if (it == c.kids.end()) break;
+      const Node& k = nodes[it->second];
+      int64_t m = 0;
+      while (m < int64_t(k.edge.size()) && depth + m < n && k.edge[m] == t[depth + m]) ++m;
+      if (segs) segs->push_back({it->second, depth, depth + m});
+      depth += m;
+      if (m < int64_t(k.edge.size())) {  // stopped inside this edge
+        if (stop_node) *stop_node = it->second;
+        if (stop_off) *stop_off = m;
+        return depth;
+      }
+      cur = it->second;
+      if (stop_node) *stop_node = cur;
+      if (stop_off) *stop_off = int64_t(k.edge.size());
+    }
+    return depth;
+  }
+
+  // Blocks of a hit of h tokens along the segments of its walk.
+  void hit_blocks(const std::vector<Seg>& segs, int64_t h, std::vector<int32_t>* out) const {
+    const int32_t bs = alloc->block_size;
+    size_t s = 0;
+    for (int64_t j = 0; j < pa_alloc::blocks_for(h, bs); ++j) {
+      const int64_t q = std::min<int64_t>((j + 1) * bs, h) - 1;
+      while (segs[s].hi <= q) ++s;
+      out->push_back(entries[nodes[segs[s].node].creator].table[j]);
+    }
+  }
+
+  void release(int32_t b) {
+    if (--alloc->refs[b] == 0) alloc->give_back(b);
+  }
+};
+
+extern "C" {
+
+pa_status pa_prefix_index_create(pa_allocator* a, pa_prefix_index** out) {
+  if (!out || !a) return pa::fail(PA_ERR_INVALID, "pa_prefix_index_create: NULL argument");
+  *out = nullptr;
+  pa_prefix_index* x = new (std::nothrow) pa_prefix_index();
+  if (!x) return pa::fail(PA_ERR_OOM, "pa_prefix_index_create: host allocation failed");
+  x->alloc = a;
+  x->nodes.emplace_back();
+  *out = x;
+  return PA_OK;
+}
+
+pa_status pa_prefix_clear(pa_prefix_index* x) {
+  if (!x) return pa::fail(PA_ERR_INVALID, "pa_prefix_clear: index is NULL");
+  for (const Entry& e : x->entries)
+    for (int32_t b : e.refs) x->release(b);
+  x->entries.clear();
+  x->nodes.clear();
+  x->nodes.emplace_back();
+  return PA_OK;
+}
+
+void pa_prefix_index_destroy(pa_prefix_index* x) {
+  if (!x) return;
+  pa_prefix_clear(x);
+  delete x;
+}
+
+pa_status pa_prefix_insert(pa_prefix_index* x, int64_t seq_id, const int32_t* tokens,
+                           int32_t num_tokens, int32_t* divergence) {
+  if (!x || (!tokens && num_tokens > 0) || num_tokens < 0)
+    return pa::fail(PA_ERR_INVALID, "pa_prefix_insert: bad argument");
+  pa_allocator* a = x->alloc;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end())
+    return pa::fail(PA_ERR_NO_SEQ, "pa_prefix_insert: no sequence %lld", (long long)seq_id);
+  const pa_alloc::Sequence& s = it->second;
+  if (num_tokens > s.len)
+    return pa::fail(PA_ERR_INVALID, "pa_prefix_insert: %d tokens, sequence holds %lld",
+                    num_tokens, (long long)s.len);
+  const int32_t bs = a->block_size;
+  const int64_t n = num_tokens;
+  try {
+    int32_t stop_node = 0;
+    int64_t stop_off = 0;
+    const int64_t d = x->walk(tokens, n, nullptr, &stop_node, &stop_off);
+    Entry e;
+    e.table.assign(s.table.begin(), s.table.begin() + pa_alloc::blocks_for(n, bs));
+    if (d < n)
+      for (int64_t j = d / bs; j <= (n - 1) / bs; ++j) e.refs.push_back(e.table[j]);
+    const int32_t eid = int32_t(x->entries.size());
+    x->nodes.reserve(x->nodes.size() + 2);
+    x->entries.reserve(x->entries.size() + 1);
+    if (d < n) {
+      int32_t parent = stop_node;
+      if (stop_node != 0 && stop_off < int64_t(x->nodes[stop_node].edge.size())) {
+        // Split the edge: a new upper node keeps edge[0, off) and the creator.
+        Node& low = x->nodes[stop_node];
+        Node up;
+        up.edge.assign(low.edge.begin(), low.edge.begin() + stop_off);
+        up.start = low.start;
+        up.creator = low.creator;
+        up.parent = low.parent;
+        const int32_t up_id = int32_t(x->nodes.size());
+        x->nodes[low.parent].kids[low.edge[0]] = up_id;  // the parent's link now points at up
+        up.kids[low.edge[stop_off]] = stop_node;
+        low.parent = up_id;
+        low.edge.erase(low.edge.begin(), low.edge.begin() + stop_off);
+        low.start += stop_off;
+        x->nodes.push_back(std::move(up));
+        parent = up_id;
+      }
+      Node leaf;
+      leaf.edge.assign(tokens + d, tokens + n);
+      leaf.start = d;
+      leaf.creator = eid;
+      leaf.parent = parent;
+      const int32_t leaf_id = int32_t(x->nodes.size());
+      x->nodes.push_back(std::move(leaf));
+      x->nodes[parent].kids[tokens[d]] = leaf_id;
+    }
+    for (int32_t b : e.refs) ++a->refs[b];
+    x->entries.push_back(std::move(e));
+    if (divergence) *divergence = int32_t(d);
+  } catch (const std::bad_alloc&) {
+    return pa::fail(PA_ERR_OOM, "pa_prefix_insert: host allocation failed");
+  }
+  return PA_OK;
+}
+
+pa_status pa_prefix_match(const pa_prefix_index* x, const int32_t* tokens, int32_t num_tokens,
+                          int32_t* hit_len) {
+  if (!x || !hit_len || (!tokens && num_tokens > 0) || num_tokens < 0)
+    return pa::fail(PA_ERR_INVALID, "pa_prefix_match: bad argument");
+  *hit_len = int32_t(x->walk(tokens, num_tokens, nullptr, nullptr, nullptr));
+  return PA_OK;
+}
+
+pa_status pa_alloc_prompt_cached(pa_prefix_index* x, int64_t seq_id, const int32_t* tokens,
+                                 int32_t num_tokens, int32_t* hit_len, int64_t* slots_out,
+                                 int32_t* cow_src_dst, int32_t* num_cow) {
+  if (!x || (!tokens && num_tokens > 0) || num_tokens < 0)
+    return pa::fail(PA_ERR_INVALID, "pa_alloc_prompt_cached: bad argument");
+  pa_allocator* a = x->alloc;
+  if (a->seqs.count(seq_id))
+    return pa::fail(PA_ERR_INVALID, "pa_alloc_prompt_cached: sequence %lld exists",
+                    (long long)seq_id);
+  const int32_t bs = a->block_size;
+  try {
+    std::vector<Seg> segs;
+    const int64_t h = x->walk(tokens, num_tokens, &segs, nullptr, nullptr);
+    const bool cow = num_tokens > h && h % bs != 0;
+    const int64_t need = pa_alloc::blocks_for(num_tokens, bs) - pa_alloc::blocks_for(h, bs) +
+                         (cow ? 1 : 0);
+    if (need > a->count) {
+      ++a->oom_refusals;
+      return pa::fail(PA_ERR_OOM, "OOM: cached prompt needs %lld blocks, %lld free",
+                      (long long)need, (long long)a->count);
+    }
+    pa_alloc::Sequence s;
+    x->hit_blocks(segs, h, &s.table);
+    s.table.reserve(pa_alloc::blocks_for(num_tokens, bs) + 1);
+    s.len = h;
+    auto ins = a->seqs.emplace(seq_id, std::move(s));
+    for (int32_t b : ins.first->second.table) ++a->refs[b];
+    int32_t pair[2];
+    a->apply_append(ins.first->second, num_tokens - h, slots_out, pair);
+    if (cow_src_dst) {
+      cow_src_dst[0] = pair[0];
+      cow_src_dst[1] = pair[1];
+    }
+    if (num_cow) *num_cow = pair[0] >= 0 ? 1 : 0;
+    if (hit_len) *hit_len = int32_t(h);
+  } catch (const std::bad_alloc&) {
+    return pa::fail(PA_ERR_OOM, "pa_alloc_prompt_cached: host allocation failed");
+  }
+  return PA_OK;
+}
+
+pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out3) {
+  if (!x || !out3) return pa::fail(PA_ERR_INVALID, "pa_prefix_stats: NULL argument");
+  int64_t refs = 0;
+  for (const Entry& e : x->entries) refs += int64_t(e.refs.size());
+  out3[0] = int64_t(x->entries.size());
+  out3[1] = int64_t(x->nodes.size());
+  out3[2] = refs;
+  return PA_OK;
+}
+
+}  // extern "C"
