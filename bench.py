@@ -328,6 +328,78 @@ class DecodeBench:
                 "unique_GBps": self.unique_bytes(lens) / t / 1e9,
                 "flush": f"{flush_mib} MiB device read before each of {reps} calls"}
 
+    def prefix_reuse(self, reps=5):
+        """Prefill of the workload's 64 prompts (the shared 1024-token prefix,
+        then each sequence's own tokens; token ids drawn from the seed) in
+        two ways on one pool: every prompt in full, and through the prefix
+        index -- request 0 in full and inserted, the other 63 allocated from
+        the cache and prefilled on their own tokens only (queries against the
+        whole prompt's context).  Event-timed prefill per way; host time per
+        index call (C++ through ctypes)."""
+        cfg = self.cfg
+        H, D, bs, B, P = self.H, self.D, self.bs, self.B, cfg["prefix"]
+        rng = np.random.default_rng(cfg["seed"])
+        system = [int(t) for t in rng.integers(0, 32000, P)]
+        own = W.uniform_ints(cfg["seed"], B, cfg["suffix_lo"], cfg["suffix_hi"])
+        prompts = [system + [int(t) for t in rng.integers(0, 32000, int(n))] for n in own]
+        N = sum(-(-len(p) // bs) for p in prompts) + 8
+        pool = pa.PagedPool.empty(N, H, bs, D, "bf16", self.device)
+        pool.k_cache.normal_()
+        pool.v_cache.normal_()
+        tdt = pa.TORCH_DTYPE["bf16"]
+
+        def run(seqs, alloc, qlens):
+            t, ln = alloc.pack(seqs, max(len(alloc.block_table(s_)) for s_ in seqs))
+            qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+            q = torch.randn((int(qsl[-1]), H, D), device=self.device).to(tdt)
+            out = torch.empty_like(q)
+            args = (out, q, pool, torch.from_numpy(t).to(self.device),
+                    torch.from_numpy(ln).to(self.device), torch.from_numpy(qsl).to(self.device),
+                    int(max(qlens)), self.scale)
+            pa.pa_prefill_chunk(*args)
+            ts = []
+            for _ in range(reps):
+                tm = Timer()
+                tm.start()
+                pa.pa_prefill_chunk(*args)
+                tm.stop()
+                torch.cuda.synchronize()
+                ts.append(tm.seconds())
+            return float(np.median(ts)), int(qsl[-1])
+
+        a_full = pa.Allocator(N, bs)
+        for i, p_ in enumerate(prompts):
+            a_full.alloc_prompt(i, len(p_))
+        t_full, q_full = run(list(range(B)), a_full, [len(p_) for p_ in prompts])
+        del a_full
+
+        a = pa.Allocator(N, bs)
+        x = pa.PrefixIndex(a)
+        a.alloc_prompt(0, len(prompts[0]))
+        t0 = time.perf_counter()
+        x.insert(0, prompts[0])
+        t_insert = time.perf_counter() - t0
+        t_match = t_alloc = 0.0
+        hits = []
+        for i in range(1, B):
+            t0 = time.perf_counter()
+            x.match(prompts[i])
+            t_match += time.perf_counter() - t0
+            t0 = time.perf_counter()
+            hit, _, _ = x.alloc_prompt_cached(i, prompts[i])
+            t_alloc += time.perf_counter() - t0
+            hits.append(hit)
+        qlens = [len(prompts[0])] + [len(prompts[i]) - hits[i - 1] for i in range(1, B)]
+        t_cached, q_cached = run(list(range(B)), a, qlens)
+        del x, a, pool
+        torch.cuda.empty_cache()
+        return {"requests": B, "prefix_tokens": P, "hits": sorted(set(hits)),
+                "query_tokens": {"full": q_full, "cached": q_cached},
+                "prefill_us": {"full": t_full * 1e6, "cached": t_cached * 1e6},
+                "speedup": t_full / t_cached,
+                "host_us_per_call": {"insert": t_insert * 1e6, "match": t_match / (B - 1) * 1e6,
+                                     "alloc_prompt_cached": t_alloc / (B - 1) * 1e6}}
+
     def cow_copy_us(self, reps=10):
         """One copy-on-write block copy as the allocator issues it: fork a
         sequence whose last block is partly filled, append one token (one
@@ -635,6 +707,8 @@ def main():
             res["unique_bytes_per_launch"] = ub
             res["unique_GBps"] = ub / kt / 1e9
             res["cow_copy"] = b.cow_copy_us()
+            log("bench: prefix reuse")
+            res["prefix_reuse"] = b.prefix_reuse()
     if not args.no_cpu_baseline:
         log("bench: cpu baseline")
         res["cpu_baseline"] = b.cpu_baseline()
