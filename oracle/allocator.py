@@ -60,6 +60,28 @@ class OracleAllocator:
         self.lens = {}
         self.cow_copies = 0
         self.oom_count = 0
+        # a prefix index with eviction (oracle/radix.py) registers itself here;
+        # an allocation that would run out asks it to reclaim blocks first
+        self.evictor = None
+
+    def _short(self, demand):
+        """True if the blocks an operation needs cannot be had.  demand(alloc)
+        is that need in a given state: an eviction can lower it (a block that
+        loses its index reference needs no copy any more), so the evictor
+        re-evaluates it after each eviction."""
+        if len(self.free) >= demand(self):
+            return False
+        return self.evictor is None or not self.evictor.reclaim(
+            lambda a: len(a.free) >= demand(a))
+
+    def _append_demand(self, seq_id, k, dropped=None):
+        """Blocks an append of k tokens to seq_id needs now: growth, plus one
+        for a copy when its last block is partly filled and still shared
+        (dropped: references a batch's earlier copies take off blocks)."""
+        table, L, bs = self.tables[seq_id], self.lens[seq_id], self.block_size
+        refs = self.refcount[table[-1]] - (dropped or {}).get(table[-1], 0) if table else 0
+        cow = k > 0 and L % bs != 0 and refs > 1
+        return ceil_div(L + k, bs) - ceil_div(L, bs) + (1 if cow else 0), cow
 
     # -- helpers -----------------------------------------------------------
     def _take(self):
@@ -84,7 +106,7 @@ class OracleAllocator:
         if num_tokens < 0:
             raise ValueError("negative length")
         need = ceil_div(num_tokens, self.block_size)
-        if len(self.free) < need:
+        if self._short(lambda a: need):
             self.oom_count += 1
             raise OOMError()
         self.tables[seq_id] = [self._take() for _ in range(need)]
@@ -97,14 +119,14 @@ class OracleAllocator:
             raise KeyError(seq_id)
         if k < 0:
             raise ValueError("negative count")
+        if self._short(lambda a: a._append_demand(seq_id, k)[0]):
+            self.oom_count += 1
+            raise OOMError()
         table = self.tables[seq_id]
         L = self.lens[seq_id]
         bs = self.block_size
-        needs_cow = k > 0 and L % bs != 0 and self.refcount[table[-1]] > 1
         grow = ceil_div(L + k, bs) - ceil_div(L, bs)
-        if len(self.free) < grow + (1 if needs_cow else 0):
-            self.oom_count += 1
-            raise OOMError()
+        needs_cow = self._append_demand(seq_id, k)[1]
         cow = None
         if needs_cow:
             src = table[-1]
@@ -117,6 +139,33 @@ class OracleAllocator:
             table.append(self._take())
         self.lens[seq_id] = L + k
         return self._slots(seq_id, L, L + k), cow
+
+    def append_tokens_batch(self, seq_ids, k=1):
+        """k tokens appended to each listed sequence in order, all or nothing:
+        the whole demand is checked first (a copy made for an earlier
+        sequence drops its reference, which a later sequence sharing that
+        block sees).  Returns [(slots, cow) per sequence]."""
+        seq_ids = list(seq_ids)
+        if len(set(seq_ids)) != len(seq_ids):
+            raise ValueError("sequence listed twice")
+        for s in seq_ids:
+            if s not in self.tables:
+                raise KeyError(s)
+
+        def demand(a):
+            dropped, need = {}, 0
+            for s in seq_ids:
+                n, cow = a._append_demand(s, k, dropped)
+                need += n
+                if cow:
+                    last = a.tables[s][-1]
+                    dropped[last] = dropped.get(last, 0) + 1
+            return need
+
+        if self._short(demand):
+            self.oom_count += 1
+            raise OOMError()
+        return [self.append_tokens(s, k) for s in seq_ids]
 
     def fork(self, parent_id, child_id):
         """Child shares every block of the parent (refcount + 1)."""
