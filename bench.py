@@ -400,6 +400,64 @@ class DecodeBench:
                 "host_us_per_call": {"insert": t_insert * 1e6, "match": t_match / (B - 1) * 1e6,
                                      "alloc_prompt_cached": t_alloc / (B - 1) * 1e6}}
 
+    def eviction_churn(self, requests=2000, systems=16, live_max=16, generated=128):
+        """Host-side serving churn on the workload's pool geometry (block 16,
+        4096 blocks): requests are one of `systems` 1024-token system prompts
+        plus 1..256 own tokens; each is allocated through the prefix index,
+        grows by `generated` tokens, and when it finishes (oldest first, at
+        most live_max in flight) is inserted whole and freed.  Finished
+        conversations fill the pool with cached blocks; with automatic
+        eviction the least recently used leaves make room, without it the
+        allocator refuses.  Host time per index call (C++ through ctypes)."""
+        cfg, bs, N = self.cfg, self.bs, self.cfg["num_blocks"]
+        rng = np.random.default_rng(cfg["seed"] + 1)
+        sys_prompts = [[int(t) for t in rng.integers(0, 32000, cfg["prefix"])] for _ in range(systems)]
+        reqs = [(int(rng.integers(0, systems)), [int(t) for t in rng.integers(0, 32000, int(n))])
+                for n in rng.integers(cfg["suffix_lo"], cfg["suffix_hi"] + 1, requests)]
+        out = {"requests": requests, "systems": systems, "pool_blocks": N, "live_max": live_max}
+        for mode in ("evict", "no_evict"):
+            a = pa.Allocator(N, bs)
+            x = pa.PrefixIndex(a, auto_evict=(mode == "evict"))
+            live, toks = [], {}
+            refused = hit_tok = prompt_tok = 0
+            t_alloc = t_ins = 0.0
+            n_alloc = n_ins = 0
+            for i, (sp, own) in enumerate(reqs):
+                if len(live) >= live_max:
+                    s = live.pop(0)
+                    t0 = time.perf_counter()
+                    x.insert(s, toks.pop(s))
+                    t_ins += time.perf_counter() - t0
+                    n_ins += 1
+                    a.free_seq(s)
+                p = sys_prompts[sp] + own
+                t0 = time.perf_counter()
+                try:
+                    hit, _, _ = x.alloc_prompt_cached(i, p)
+                except RuntimeError:
+                    refused += 1
+                    continue
+                finally:
+                    t_alloc += time.perf_counter() - t0
+                    n_alloc += 1
+                hit_tok += hit
+                prompt_tok += len(p)
+                try:
+                    a.append_tokens(i, generated)
+                except RuntimeError:
+                    refused += 1
+                    a.free_seq(i)
+                    continue
+                live.append(i)
+                toks[i] = p + [int(t) for t in rng.integers(0, 32000, generated)]
+            st = x.stats()
+            out[mode] = {"refused": refused, "evicted_leaves": st["evicted"],
+                         "hit_token_fraction": hit_tok / max(prompt_tok, 1),
+                         "host_us_per_call": {"alloc_prompt_cached": t_alloc / max(n_alloc, 1) * 1e6,
+                                              "insert": t_ins / max(n_ins, 1) * 1e6}}
+            del x, a
+        return out
+
     def cow_copy_us(self, reps=10):
         """One copy-on-write block copy as the allocator issues it: fork a
         sequence whose last block is partly filled, append one token (one
@@ -709,6 +767,8 @@ def main():
             res["cow_copy"] = b.cow_copy_us()
             log("bench: prefix reuse")
             res["prefix_reuse"] = b.prefix_reuse()
+            log("bench: eviction churn (host)")
+            res["eviction"] = b.eviction_churn()
     if not args.no_cpu_baseline:
         log("bench: cpu baseline")
         res["cpu_baseline"] = b.cpu_baseline()

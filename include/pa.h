@@ -278,6 +278,16 @@ pa_status pa_allocator_stats(const pa_allocator* a, int64_t* out5);
  * (indices d / bs .. (n-1) / bs), so cached blocks outlive the sequence.
  * Block j of a hit of h tokens is block j of the earliest entry whose common
  * prefix with the prompt is longer than min((j+1) * bs, h) - 1.
+ *
+ * Eviction (the same section's LRU rule for a full memory: leaves of the
+ * tree go first, least recently used first, until there is room).  Every
+ * pa_prefix_insert and pa_alloc_prompt_cached stamps the tree nodes its walk
+ * entered with a logical clock (pa_prefix_match stamps nothing); the oldest
+ * leaf goes first, ties to the older node.  Evicting a leaf drops its
+ * creating entry's references on the blocks only that leaf uses (the block
+ * under its first position stays when the parent node, made by the same
+ * entry, also lies in it); a block left with no reference goes back to the
+ * free list.  Blocks of live sequences are never taken.
  */
 typedef struct pa_prefix_index pa_prefix_index;
 
@@ -311,8 +321,26 @@ pa_status pa_alloc_prompt_cached(pa_prefix_index* x, int64_t seq_id, const int32
  * list in that order). */
 pa_status pa_prefix_clear(pa_prefix_index* x);
 
-/* [0] entries, [1] tree nodes (root included), [2] block references held. */
-pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out3);
+/* [0] entries, [1] live tree nodes (root included), [2] block references
+ * held, [3] leaves evicted so far. */
+pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out4);
+
+/* Switch automatic eviction on (enable != 0) or off for x.  While on, an
+ * allocating call on x's allocator (pa_alloc_prompt, pa_append_tokens,
+ * pa_append_tokens_batch, pa_alloc_prompt_cached) that would run out of
+ * blocks first evicts leaves of x until its demand fits, re-evaluating the
+ * demand after every eviction (a block that loses the index's reference may
+ * need no copy any more); pa_alloc_prompt_cached never evicts the nodes of
+ * its own hit.  If evicting every other leaf would not be enough, the
+ * evictions are undone and the call fails with PA_ERR_OOM, nothing changed.
+ * One evicting index per allocator: PA_ERR_INVALID if another has it on.
+ * Off by default (the allocator then reports OOM when its free list is
+ * short). */
+pa_status pa_prefix_set_auto_evict(pa_prefix_index* x, int32_t enable);
+
+/* Evict oldest leaves until the allocator has min_free_blocks free blocks
+ * or no leaf is left; *num_evicted (may be NULL) receives the count. */
+pa_status pa_prefix_evict(pa_prefix_index* x, int64_t min_free_blocks, int64_t* num_evicted);
 
 const char* pa_last_error(void);
 

@@ -43,6 +43,7 @@ EXPORTS = [
     "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
     "pa_prefix_index_create", "pa_prefix_index_destroy", "pa_prefix_insert", "pa_prefix_match",
     "pa_alloc_prompt_cached", "pa_prefix_clear", "pa_prefix_stats",
+    "pa_prefix_set_auto_evict", "pa_prefix_evict",
     "pa_last_error",
 ]
 
@@ -93,6 +94,8 @@ def _load():
         "pa_alloc_prompt_cached": (I32, [VP, I64, pi32, I32, pi32, pi64, pi32, pi32]),
         "pa_prefix_clear": (I32, [VP]),
         "pa_prefix_stats": (I32, [VP, pi64]),
+        "pa_prefix_set_auto_evict": (I32, [VP, I32]),
+        "pa_prefix_evict": (I32, [VP, I64, pi64]),
         "pa_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -384,13 +387,25 @@ class PrefixIndex:
     tree): insert cached sequences, match prompts, allocate a prompt that
     reuses its longest cached prefix.  Keeps the allocator alive."""
 
-    def __init__(self, alloc):
+    def __init__(self, alloc, auto_evict=False):
         import numpy as np
         self._np = np
         self.alloc = alloc
         h = ctypes.c_void_p()
         _check(lib.pa_prefix_index_create(alloc._h, ctypes.byref(h)), "pa_prefix_index_create")
         self._h = h
+        if auto_evict:
+            self.set_auto_evict(True)
+
+    def set_auto_evict(self, enable):
+        """Evict least recently used leaves when an allocation would run out."""
+        _check(lib.pa_prefix_set_auto_evict(self._h, 1 if enable else 0), "pa_prefix_set_auto_evict")
+
+    def evict(self, min_free_blocks):
+        """Evict oldest leaves until min_free_blocks are free; returns how many."""
+        n = ctypes.c_int64()
+        _check(lib.pa_prefix_evict(self._h, min_free_blocks, ctypes.byref(n)), "pa_prefix_evict")
+        return n.value
 
     def __del__(self, _destroy=lib.pa_prefix_index_destroy):
         h = getattr(self, "_h", None)
@@ -432,7 +447,8 @@ class PrefixIndex:
         _check(lib.pa_prefix_clear(self._h), "pa_prefix_clear")
 
     def stats(self):
-        out = self._np.zeros(3, dtype=self._np.int64)
+        out = self._np.zeros(4, dtype=self._np.int64)
         _check(lib.pa_prefix_stats(self._h, _i64p(out)), "pa_prefix_stats")
-        return {"entries": int(out[0]), "nodes": int(out[1]), "referenced_blocks": int(out[2])}
+        return {"entries": int(out[0]), "nodes": int(out[1]), "referenced_blocks": int(out[2]),
+                "evicted": int(out[3])}
 

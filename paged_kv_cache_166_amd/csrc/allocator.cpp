@@ -72,7 +72,7 @@ pa_status pa_alloc_prompt(pa_allocator* a, int64_t seq_id, int32_t num_tokens,
   if (a->seqs.count(seq_id))
     return pa::fail(PA_ERR_INVALID, "pa_alloc_prompt: sequence %lld exists", (long long)seq_id);
   int64_t need = blocks_for(num_tokens, a->block_size);
-  if (need > a->count) {
+  if (a->short_of([&] { return need; })) {
     ++a->oom_refusals;
     return pa::fail(PA_ERR_OOM, "OOM: prompt needs %lld blocks, %lld free", (long long)need,
                     (long long)a->count);
@@ -94,10 +94,12 @@ pa_status pa_append_tokens(pa_allocator* a, int64_t seq_id, int32_t n, int64_t* 
   if (it == a->seqs.end())
     return pa::fail(PA_ERR_NO_SEQ, "pa_append_tokens: no sequence %lld", (long long)seq_id);
   Sequence& s = it->second;
-  bool cow = false;
-  int32_t last_refs = s.table.empty() ? 0 : a->refs[s.table.back()];
-  int64_t need = a->demand(s, n, last_refs, &cow);
-  if (need > a->count) {
+  auto need_now = [&] {
+    bool cow = false;
+    return a->demand(s, n, s.table.empty() ? 0 : a->refs[s.table.back()], &cow);
+  };
+  if (a->short_of(need_now)) {
+    const int64_t need = need_now();
     ++a->oom_refusals;
     return pa::fail(PA_ERR_OOM, "OOM: append needs %lld blocks, %lld free", (long long)need,
                     (long long)a->count);
@@ -118,11 +120,8 @@ pa_status pa_append_tokens_batch(pa_allocator* a, const int64_t* seq_ids, int32_
   if (!a || (!seq_ids && num_seqs > 0))
     return pa::fail(PA_ERR_INVALID, "pa_append_tokens_batch: NULL argument");
   if (n < 0 || num_seqs < 0) return pa::fail(PA_ERR_INVALID, "pa_append_tokens_batch: negative size");
-  // Dry run: the reference counts the batch's own copies leave behind decide
-  // whether a later sequence of the batch still shares its last block.
   std::unordered_set<int64_t> ids;
-  std::unordered_map<int32_t, int32_t> dropped;
-  int64_t need = 0;
+  std::vector<const Sequence*> listed(num_seqs);
   for (int32_t i = 0; i < num_seqs; ++i) {
     if (!ids.insert(seq_ids[i]).second)
       return pa::fail(PA_ERR_INVALID, "pa_append_tokens_batch: sequence %lld listed twice",
@@ -131,14 +130,25 @@ pa_status pa_append_tokens_batch(pa_allocator* a, const int64_t* seq_ids, int32_
     if (it == a->seqs.end())
       return pa::fail(PA_ERR_NO_SEQ, "pa_append_tokens_batch: no sequence %lld",
                       (long long)seq_ids[i]);
-    const Sequence& s = it->second;
-    int32_t last = s.table.empty() ? -1 : s.table.back();
-    int32_t last_refs = last < 0 ? 0 : a->refs[last] - (dropped.count(last) ? dropped[last] : 0);
-    bool cow = false;
-    need += a->demand(s, n, last_refs, &cow);
-    if (cow) ++dropped[last];
+    listed[i] = &it->second;
   }
-  if (need > a->count) {
+  // Dry run: the reference counts the batch's own copies leave behind decide
+  // whether a later sequence of the batch still shares its last block.
+  std::unordered_map<int32_t, int32_t> dropped;
+  auto need_now = [&] {
+    dropped.clear();
+    int64_t need = 0;
+    for (const Sequence* s : listed) {
+      int32_t last = s->table.empty() ? -1 : s->table.back();
+      int32_t last_refs = last < 0 ? 0 : a->refs[last] - (dropped.count(last) ? dropped[last] : 0);
+      bool cow = false;
+      need += a->demand(*s, n, last_refs, &cow);
+      if (cow) ++dropped[last];
+    }
+    return need;
+  };
+  if (a->short_of(need_now)) {
+    const int64_t need = need_now();
     ++a->oom_refusals;
     return pa::fail(PA_ERR_OOM, "OOM: batch append needs %lld blocks, %lld free",
                     (long long)need, (long long)a->count);

@@ -3,8 +3,11 @@
 // block references through it).  Not part of the C ABI.
 #pragma once
 #include <cstdint>
+#include <functional>
 #include <unordered_map>
 #include <vector>
+
+struct pa_prefix_index;
 
 namespace pa_alloc {
 
@@ -14,6 +17,11 @@ struct Sequence {
   std::vector<int32_t> table;
   int64_t len = 0;
 };
+
+// Evicts the index's least recently used leaves until fits() holds; when
+// evicting every leaf would not be enough, undoes what it evicted and
+// returns false (defined with the index, prefix.cpp).
+bool reclaim(pa_prefix_index* x, const std::function<bool()>& fits);
 
 }  // namespace pa_alloc
 
@@ -28,6 +36,18 @@ struct pa_allocator {
   std::unordered_map<int64_t, Sequence> seqs;
   int64_t cow_copies = 0;
   int64_t oom_refusals = 0;
+  // A prefix index with automatic eviction switched on: an allocation that
+  // would run out asks it to evict cached prefixes first.
+  pa_prefix_index* evictor = nullptr;
+
+  // True when an operation cannot get its blocks.  demand() is the operation's
+  // need in the current state; an eviction can lower it (a last block that
+  // loses the index's reference needs no copy), so it is asked again after
+  // every eviction.
+  bool short_of(const std::function<int64_t()>& demand) {
+    if (demand() <= count) return false;
+    return !evictor || !pa_alloc::reclaim(evictor, [&] { return demand() <= count; });
+  }
 
   int32_t take() {
     int32_t b = ring[head];

@@ -18,10 +18,26 @@
 // tokens equal the prompt up to there, so its block j holds the right rows.
 // A hit that ends inside a block shares that partly filled block; the
 // allocator's copy-on-write copies it on the sequence's first write.
+//
+// Eviction (the notes' LRU rule: when memory is full, the KV cache of leaf
+// nodes goes first, least recently used first, until there is room): every
+// insertion and cached-prompt allocation stamps the nodes its walk entered
+// with a logical clock; a leaf is evicted whole, oldest stamp first (ties to
+// the older node); evicting it drops its creator's references on the blocks
+// only it uses -- the block under its first position stays when the parent
+// node has the same creator and also lies in it -- and blocks left with no
+// reference go back to the free list.  Live sequences keep their own
+// references, so eviction never takes their blocks.  With automatic eviction
+// switched on, an allocation that would run out evicts until it fits, on an
+// undo log: if evicting every leaf (but those of a cached prompt's own hit)
+// is not enough, the evictions are undone and the call fails unchanged.
 #include <algorithm>
 #include <cstdint>
 #include <new>
+#include <set>
 #include <unordered_map>
+#include <unordered_set>
+#include <utility>
 #include <vector>
 
 #include "allocator_impl.h"
@@ -35,12 +51,24 @@ struct Node {
   int64_t start = 0;          // depth of edge[0]
   int32_t creator = -1;       // entry whose insertion created these positions
   int32_t parent = -1;
+  uint64_t stamp = 0;         // clock of the last walk that entered it
+  bool alive = true;          // false once evicted (ids are never reused)
   std::unordered_map<int32_t, int32_t> kids;  // first token of a child's edge -> node
+  int64_t end() const { return start + int64_t(edge.size()); }
 };
 
 struct Entry {
   std::vector<int32_t> table;  // the sequence's blocks covering its n tokens
-  std::vector<int32_t> refs;   // blocks this entry holds a reference on, by index
+  int64_t ref_base = 0;        // block index of refs[0]
+  std::vector<int32_t> refs;   // block referenced at each index from ref_base, -1 once dropped
+  int64_t held = 0;            // references still held
+};
+
+// What one eviction changed, so that a failed reclaim can put it back.
+struct Evicted {
+  int32_t leaf;
+  bool parent_became_leaf;
+  std::vector<std::pair<int64_t, int32_t>> released;  // (block index, block), in order
 };
 
 // One step of a walk: node, and the depth range [lo, hi) of the prompt it
@@ -56,6 +84,19 @@ struct pa_prefix_index {
   pa_allocator* alloc = nullptr;
   std::vector<Node> nodes;  // nodes[0] is the root (empty edge)
   std::vector<Entry> entries;
+  std::set<std::pair<uint64_t, int32_t>> leaves;  // (stamp, node) of every live leaf
+  uint64_t clock = 0;
+  int64_t evicted = 0;
+
+  bool is_leaf(int32_t id) const { return id != 0 && nodes[id].alive && nodes[id].kids.empty(); }
+
+  void touch(int32_t id) {
+    if (is_leaf(id)) {
+      leaves.erase({nodes[id].stamp, id});
+      leaves.insert({clock, id});
+    }
+    nodes[id].stamp = clock;
+  }
 
   // Longest match of tokens from the root; the segments walked, and where
   // the walk stopped (node, offset in its edge) for an insertion.
@@ -100,7 +141,85 @@ struct pa_prefix_index {
   void release(int32_t b) {
     if (--alloc->refs[b] == 0) alloc->give_back(b);
   }
+
+  // Oldest live leaf not in keep, or -1.
+  int32_t oldest(const std::unordered_set<int32_t>& keep) const {
+    for (const auto& l : leaves)
+      if (!keep.count(l.second)) return l.second;
+    return -1;
+  }
+
+  Evicted evict(int32_t id) {
+    Node& L = nodes[id];
+    Node& P = nodes[L.parent];
+    Entry& e = entries[L.creator];
+    const int32_t bs = alloc->block_size;
+    int64_t first = L.start / bs;
+    if (L.start % bs != 0 && L.parent != 0 && P.creator == L.creator) ++first;
+    const int64_t last = (L.end() - 1) / bs;
+    Evicted r{id, false, {}};
+    r.released.reserve(size_t(std::max<int64_t>(last - first + 1, 0)));
+    const bool parent_leaf = L.parent != 0 && P.kids.size() == 1;
+    if (parent_leaf) leaves.insert({P.stamp, L.parent});
+    for (int64_t j = std::max(first, e.ref_base); j <= last; ++j) {
+      const int64_t k = j - e.ref_base;
+      if (k >= int64_t(e.refs.size()) || e.refs[k] < 0) continue;
+      const int32_t b = e.refs[k];
+      e.refs[k] = -1;
+      --e.held;
+      r.released.emplace_back(j, b);
+      release(b);
+    }
+    leaves.erase({L.stamp, id});
+    P.kids.erase(L.edge[0]);
+    L.alive = false;
+    r.parent_became_leaf = parent_leaf;
+    return r;
+  }
+
+  void undo(const Evicted& r) {
+    Node& L = nodes[r.leaf];
+    Node& P = nodes[L.parent];
+    Entry& e = entries[L.creator];
+    if (r.parent_became_leaf) leaves.erase({P.stamp, L.parent});
+    L.alive = true;
+    P.kids[L.edge[0]] = r.leaf;
+    leaves.insert({L.stamp, r.leaf});
+    for (auto it = r.released.rbegin(); it != r.released.rend(); ++it) {
+      const int32_t b = it->second;
+      if (alloc->refs[b] == 0) --alloc->count;  // it was the free list's last entry
+      ++alloc->refs[b];
+      e.refs[it->first - e.ref_base] = b;
+      ++e.held;
+    }
+  }
+
+  // Evict oldest leaves outside keep until fits(); all or nothing.
+  bool reclaim(const std::function<bool()>& fits, const std::unordered_set<int32_t>& keep) {
+    std::vector<Evicted> log;
+    try {
+      while (!fits()) {
+        const int32_t id = oldest(keep);
+        if (id < 0) break;
+        log.emplace_back();  // room first: evict() itself leaves nothing half done
+        log.back() = evict(id);
+      }
+    } catch (const std::bad_alloc&) {
+      for (auto it = log.rbegin(); it != log.rend(); ++it) undo(*it);
+      return false;
+    }
+    if (fits()) {
+      evicted += int64_t(log.size());
+      return true;
+    }
+    for (auto it = log.rbegin(); it != log.rend(); ++it) undo(*it);
+    return false;
+  }
 };
+
+bool pa_alloc::reclaim(pa_prefix_index* x, const std::function<bool()>& fits) {
+  return x->reclaim(fits, {});
+}
 
 extern "C" {
 
@@ -118,15 +237,18 @@ pa_status pa_prefix_index_create(pa_allocator* a, pa_prefix_index** out) {
 pa_status pa_prefix_clear(pa_prefix_index* x) {
   if (!x) return pa::fail(PA_ERR_INVALID, "pa_prefix_clear: index is NULL");
   for (const Entry& e : x->entries)
-    for (int32_t b : e.refs) x->release(b);
+    for (int32_t b : e.refs)
+      if (b >= 0) x->release(b);
   x->entries.clear();
   x->nodes.clear();
   x->nodes.emplace_back();
+  x->leaves.clear();
   return PA_OK;
 }
 
 void pa_prefix_index_destroy(pa_prefix_index* x) {
   if (!x) return;
+  if (x->alloc->evictor == x) x->alloc->evictor = nullptr;
   pa_prefix_clear(x);
   delete x;
 }
@@ -148,14 +270,20 @@ pa_status pa_prefix_insert(pa_prefix_index* x, int64_t seq_id, const int32_t* to
   try {
     int32_t stop_node = 0;
     int64_t stop_off = 0;
-    const int64_t d = x->walk(tokens, n, nullptr, &stop_node, &stop_off);
+    std::vector<Seg> segs;
+    const int64_t d = x->walk(tokens, n, &segs, &stop_node, &stop_off);
     Entry e;
     e.table.assign(s.table.begin(), s.table.begin() + pa_alloc::blocks_for(n, bs));
-    if (d < n)
+    if (d < n) {
+      e.ref_base = d / bs;
       for (int64_t j = d / bs; j <= (n - 1) / bs; ++j) e.refs.push_back(e.table[j]);
+    }
+    e.held = int64_t(e.refs.size());
     const int32_t eid = int32_t(x->entries.size());
     x->nodes.reserve(x->nodes.size() + 2);
     x->entries.reserve(x->entries.size() + 1);
+    ++x->clock;
+    for (const Seg& g : segs) x->touch(g.node);
     if (d < n) {
       int32_t parent = stop_node;
       if (stop_node != 0 && stop_off < int64_t(x->nodes[stop_node].edge.size())) {
@@ -166,6 +294,7 @@ pa_status pa_prefix_insert(pa_prefix_index* x, int64_t seq_id, const int32_t* to
         up.start = low.start;
         up.creator = low.creator;
         up.parent = low.parent;
+        up.stamp = low.stamp;
         const int32_t up_id = int32_t(x->nodes.size());
         x->nodes[low.parent].kids[low.edge[0]] = up_id;  // the parent's link now points at up
         up.kids[low.edge[stop_off]] = stop_node;
@@ -180,9 +309,12 @@ pa_status pa_prefix_insert(pa_prefix_index* x, int64_t seq_id, const int32_t* to
       leaf.start = d;
       leaf.creator = eid;
       leaf.parent = parent;
+      leaf.stamp = x->clock;
       const int32_t leaf_id = int32_t(x->nodes.size());
+      if (x->is_leaf(parent)) x->leaves.erase({x->nodes[parent].stamp, parent});
       x->nodes.push_back(std::move(leaf));
       x->nodes[parent].kids[tokens[d]] = leaf_id;
+      x->leaves.insert({x->clock, leaf_id});
     }
     for (int32_t b : e.refs) ++a->refs[b];
     x->entries.push_back(std::move(e));
@@ -217,11 +349,19 @@ pa_status pa_alloc_prompt_cached(pa_prefix_index* x, int64_t seq_id, const int32
     const bool cow = num_tokens > h && h % bs != 0;
     const int64_t need = pa_alloc::blocks_for(num_tokens, bs) - pa_alloc::blocks_for(h, bs) +
                          (cow ? 1 : 0);
-    if (need > a->count) {
+    ++x->clock;
+    bool short_of = need > a->count;
+    if (short_of && a->evictor == x) {
+      std::unordered_set<int32_t> hit_nodes;
+      for (const Seg& g : segs) hit_nodes.insert(g.node);
+      short_of = !x->reclaim([&] { return need <= a->count; }, hit_nodes);
+    }
+    if (short_of) {
       ++a->oom_refusals;
       return pa::fail(PA_ERR_OOM, "OOM: cached prompt needs %lld blocks, %lld free",
                       (long long)need, (long long)a->count);
     }
+    for (const Seg& g : segs) x->touch(g.node);
     pa_alloc::Sequence s;
     x->hit_blocks(segs, h, &s.table);
     s.table.reserve(pa_alloc::blocks_for(num_tokens, bs) + 1);
@@ -242,13 +382,50 @@ pa_status pa_alloc_prompt_cached(pa_prefix_index* x, int64_t seq_id, const int32
   return PA_OK;
 }
 
-pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out3) {
-  if (!x || !out3) return pa::fail(PA_ERR_INVALID, "pa_prefix_stats: NULL argument");
-  int64_t refs = 0;
-  for (const Entry& e : x->entries) refs += int64_t(e.refs.size());
-  out3[0] = int64_t(x->entries.size());
-  out3[1] = int64_t(x->nodes.size());
-  out3[2] = refs;
+pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out4) {
+  if (!x || !out4) return pa::fail(PA_ERR_INVALID, "pa_prefix_stats: NULL argument");
+  int64_t refs = 0, live = 0;
+  for (const Entry& e : x->entries) refs += e.held;
+  for (const Node& nd : x->nodes) live += nd.alive ? 1 : 0;
+  out4[0] = int64_t(x->entries.size());
+  out4[1] = live;
+  out4[2] = refs;
+  out4[3] = x->evicted;
+  return PA_OK;
+}
+
+pa_status pa_prefix_set_auto_evict(pa_prefix_index* x, int32_t enable) {
+  if (!x) return pa::fail(PA_ERR_INVALID, "pa_prefix_set_auto_evict: index is NULL");
+  pa_allocator* a = x->alloc;
+  if (enable) {
+    if (a->evictor && a->evictor != x)
+      return pa::fail(PA_ERR_INVALID,
+                      "pa_prefix_set_auto_evict: the allocator already has an evicting index");
+    a->evictor = x;
+  } else if (a->evictor == x) {
+    a->evictor = nullptr;
+  }
+  return PA_OK;
+}
+
+pa_status pa_prefix_evict(pa_prefix_index* x, int64_t min_free_blocks, int64_t* num_evicted) {
+  if (!x) return pa::fail(PA_ERR_INVALID, "pa_prefix_evict: index is NULL");
+  int64_t n = 0;
+  try {
+    const std::unordered_set<int32_t> none;
+    while (x->alloc->count < min_free_blocks) {
+      const int32_t id = x->oldest(none);
+      if (id < 0) break;
+      x->evict(id);
+      ++n;
+    }
+  } catch (const std::bad_alloc&) {
+    x->evicted += n;
+    if (num_evicted) *num_evicted = n;
+    return pa::fail(PA_ERR_OOM, "pa_prefix_evict: host allocation failed");
+  }
+  x->evicted += n;
+  if (num_evicted) *num_evicted = n;
   return PA_OK;
 }
 
