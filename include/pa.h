@@ -17,7 +17,7 @@
  *   message for the last failing call of the calling thread.  Faults inside a
  *   kernel surface at the caller's next synchronisation of the stream.
  * - Host-side checks: null pointers, dtype combinations, head_dim in {64,128},
- *   block_size in {4,8,16,32}, 16-byte alignment of every device pointer,
+ *   block_size in {4,8,16,32,64}, 16-byte alignment of every device pointer,
  *   workspace size.  Block-table entries and slots are trusted: the caller
  *   keeps them in [0, num_blocks) (the allocator below produces only such).
  * - Pool layout: K and V are each [num_blocks][num_heads][block_size][head_dim]
@@ -66,7 +66,7 @@ typedef struct pa_pool {
   float* v_scale;     /* [num_blocks][num_heads], fp8 pools only, else NULL */
   int32_t num_blocks;
   int32_t num_heads;
-  int32_t block_size; /* tokens per block: 4, 8, 16 or 32 */
+  int32_t block_size; /* tokens per block: 4, 8, 16, 32 or 64 */
   int32_t head_dim;   /* 64 or 128 */
   int32_t kv_dtype;   /* pa_dtype */
   int32_t flags;      /* PA_POOL_* bits, 0 for none */
@@ -341,6 +341,75 @@ pa_status pa_prefix_set_auto_evict(pa_prefix_index* x, int32_t enable);
 /* Evict oldest leaves until the allocator has min_free_blocks free blocks
  * or no leaf is left; *num_evicted (may be NULL) receives the count. */
 pa_status pa_prefix_evict(pa_prefix_index* x, int64_t min_free_blocks, int64_t* num_evicted);
+
+/* ------------------------------------- host allocator, block size per request */
+
+/*
+ * One arena per layer shared by blocks of 8, 16, 32 and 64 tokens, the block
+ * size following the request's length (the first page's "3.0" feature list:
+ * page size adjusted to the request, blocks of different sizes for requests
+ * of different lengths).  The arena is a binary buddy system of 8-token
+ * units: a block of b tokens is b/8 units starting at a multiple of b/8.
+ * Pool views: for each b the same K and V memory is a pa_pool of block_size
+ * b and num_blocks arena_tokens / b, and block id i of that view is units
+ * [i*b/8, (i+1)*b/8).  A sequence's table holds block ids of the view of its
+ * own size, so pa_reshape_and_cache, pa_copy_blocks, pa_decode and
+ * pa_prefill_chunk run on that view unchanged (a batch mixing sizes is one
+ * call per size).  fp8 arenas need one scale array per view ([arena_tokens /
+ * b][heads]); a block's scales live in the array of its view.
+ *
+ * Size rule (pa_buddy_size_for): the largest b with b <= n / 16, at least 8:
+ * a request starts with 16 or more blocks, so its unfilled tail is under
+ * 1/16 of it.  A sequence keeps its size for life.
+ *
+ * Free lists: one FIFO per size; the arena starts as its 64-token blocks in
+ * top_order (NULL: ascending).  A request for size b takes the front of the
+ * b list, else splits the front of the nearest larger non-empty list,
+ * keeping the lower half and putting each upper half at the back of the list
+ * below; a freed block merges with its buddy while the buddy is free at the
+ * same size, then goes to the back of its list.  Reference counts, fork,
+ * copy-on-write and the all-or-nothing rule are those of pa_allocator; slots
+ * are block_id * b + offset in the sequence's view.  Not thread-safe.
+ */
+typedef struct pa_buddy_allocator pa_buddy_allocator;
+
+/* arena_tokens: a positive multiple of 64. */
+pa_status pa_buddy_create(int64_t arena_tokens, const int32_t* top_order, pa_buddy_allocator** out);
+void pa_buddy_destroy(pa_buddy_allocator* a);
+/* The size rule: block size for a request of num_tokens tokens. */
+int32_t pa_buddy_size_for(int64_t num_tokens);
+/* New sequence of num_tokens tokens in blocks of block_size (0: the size
+ * rule); *block_size_out (may be NULL) receives the size, slots_out (may be
+ * NULL) num_tokens slots in that size's view. */
+pa_status pa_buddy_alloc_prompt(pa_buddy_allocator* a, int64_t seq_id, int32_t num_tokens,
+                                int32_t block_size, int32_t* block_size_out, int64_t* slots_out);
+/* As pa_append_tokens, in the sequence's view. */
+pa_status pa_buddy_append_tokens(pa_buddy_allocator* a, int64_t seq_id, int32_t n,
+                                 int64_t* slots_out, int32_t* cow_src_dst, int32_t* num_cow);
+/* As pa_append_tokens_batch (sequences of any sizes; each row of slots_out
+ * and each pair in its own sequence's view). */
+pa_status pa_buddy_append_tokens_batch(pa_buddy_allocator* a, const int64_t* seq_ids,
+                                       int32_t num_seqs, int32_t n, int64_t* slots_out,
+                                       int32_t* cow_pairs_out, int32_t* num_cow);
+pa_status pa_buddy_fork(pa_buddy_allocator* a, int64_t parent_id, int64_t child_id);
+pa_status pa_buddy_free_seq(pa_buddy_allocator* a, int64_t seq_id);
+/* As pa_get_block_table; *block_size (may be NULL) receives the sequence's size. */
+pa_status pa_buddy_get_block_table(const pa_buddy_allocator* a, int64_t seq_id, int32_t* out,
+                                   int32_t cap, int32_t* len, int32_t* seq_len,
+                                   int32_t* block_size);
+/* As pa_pack_block_tables; every listed sequence must have the same size
+ * (else PA_ERR_INVALID). */
+pa_status pa_buddy_pack_block_tables(const pa_buddy_allocator* a, const int64_t* seq_ids,
+                                     int32_t num_seqs, int32_t max_blocks, int32_t* tables_out,
+                                     int32_t* lens_out);
+/* Free tokens (sum over the free lists). */
+int64_t pa_buddy_free_tokens(const pa_buddy_allocator* a);
+/* The free list of one size, front first, as block ids of that size's view
+ * (up to cap of them in out; *len receives the full length). */
+pa_status pa_buddy_free_list(const pa_buddy_allocator* a, int32_t block_size, int32_t* out,
+                             int32_t cap, int32_t* len);
+/* Reference count of block block_id of the block_size view (-1 if out of range). */
+int32_t pa_buddy_block_refcount(const pa_buddy_allocator* a, int32_t block_size, int32_t block_id);
 
 const char* pa_last_error(void);
 

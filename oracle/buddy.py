@@ -28,6 +28,7 @@ lengths, to use memory better.  Readings (listed in the design doc):
   |list j| * 2^(j-k)), copy-on-write block taken before growth blocks,
   freed blocks returned in table order, reference counts per block.
 """
+import copy
 from collections import deque
 
 from .allocator import OOMError, ceil_div
@@ -153,6 +154,25 @@ class OracleBuddyAllocator:
             table.append(self._take(k) >> k)
         self.lens[seq] = L + m
         return [self.slot(seq, p) for p in range(L, L + m)], pair
+
+    def append_tokens_batch(self, seqs, m=1):
+        """m tokens appended to each listed sequence in order, all or nothing
+        (decided by running the whole batch on a copy first).  Returns
+        [(slots, cow) per sequence]."""
+        seqs = list(seqs)
+        if len(set(seqs)) != len(seqs):
+            raise ValueError("sequence listed twice")
+        for s in seqs:
+            if s not in self.tables:
+                raise KeyError(s)
+        trial = copy.deepcopy(self)
+        try:
+            for s in seqs:
+                trial.append_tokens(s, m)
+        except OOMError:
+            self.oom_count += 1
+            raise
+        return [self.append_tokens(s, m) for s in seqs]
 
     def fork(self, parent, child):
         if parent not in self.tables:

@@ -44,6 +44,10 @@ EXPORTS = [
     "pa_prefix_index_create", "pa_prefix_index_destroy", "pa_prefix_insert", "pa_prefix_match",
     "pa_alloc_prompt_cached", "pa_prefix_clear", "pa_prefix_stats",
     "pa_prefix_set_auto_evict", "pa_prefix_evict",
+    "pa_buddy_create", "pa_buddy_destroy", "pa_buddy_size_for", "pa_buddy_alloc_prompt",
+    "pa_buddy_append_tokens", "pa_buddy_append_tokens_batch", "pa_buddy_fork", "pa_buddy_free_seq",
+    "pa_buddy_get_block_table", "pa_buddy_pack_block_tables", "pa_buddy_free_tokens",
+    "pa_buddy_free_list", "pa_buddy_block_refcount",
     "pa_last_error",
 ]
 
@@ -96,6 +100,19 @@ def _load():
         "pa_prefix_stats": (I32, [VP, pi64]),
         "pa_prefix_set_auto_evict": (I32, [VP, I32]),
         "pa_prefix_evict": (I32, [VP, I64, pi64]),
+        "pa_buddy_create": (I32, [I64, pi32, VP]),
+        "pa_buddy_destroy": (None, [VP]),
+        "pa_buddy_size_for": (I32, [I64]),
+        "pa_buddy_alloc_prompt": (I32, [VP, I64, I32, I32, pi32, pi64]),
+        "pa_buddy_append_tokens": (I32, [VP, I64, I32, pi64, pi32, pi32]),
+        "pa_buddy_append_tokens_batch": (I32, [VP, pi64, I32, I32, pi64, pi32, pi32]),
+        "pa_buddy_fork": (I32, [VP, I64, I64]),
+        "pa_buddy_free_seq": (I32, [VP, I64]),
+        "pa_buddy_get_block_table": (I32, [VP, I64, pi32, I32, pi32, pi32, pi32]),
+        "pa_buddy_pack_block_tables": (I32, [VP, pi64, I32, I32, pi32, pi32]),
+        "pa_buddy_free_tokens": (I64, [VP]),
+        "pa_buddy_free_list": (I32, [VP, I32, pi32, I32, pi32]),
+        "pa_buddy_block_refcount": (I32, [VP, I32, I32]),
         "pa_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -380,6 +397,148 @@ class Allocator:
         _check(lib.pa_allocator_stats(self._h, _i64p(out)), "pa_allocator_stats")
         return dict(used=int(out[0]), shared=int(out[1]), cow_copies=int(out[2]),
                     oom=int(out[3]), seqs=int(out[4]))
+
+
+BUDDY_SIZES = (8, 16, 32, 64)
+
+
+def buddy_size_for(num_tokens):
+    """Block size the size rule gives a request of num_tokens tokens."""
+    return int(lib.pa_buddy_size_for(num_tokens))
+
+
+class BuddyAllocator:
+    """Host allocator with a block size per request (C++ buddy system over
+    one arena of 8-token units).  Tables and slots are in the view of each
+    sequence's own block size.  OOM raises RuntimeError("OOM")."""
+
+    def __init__(self, arena_tokens, top_order=None):
+        import numpy as np
+        self._np = np
+        h = ctypes.c_void_p()
+        order = None
+        if top_order is not None:
+            order = np.ascontiguousarray(np.asarray(top_order, dtype=np.int32))
+        _check(lib.pa_buddy_create(arena_tokens, _i32p(order) if order is not None else None,
+                                   ctypes.byref(h)), "pa_buddy_create")
+        self._h = h
+        self.arena_tokens = arena_tokens
+
+    def __del__(self, _destroy=lib.pa_buddy_destroy):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _destroy(h)
+            self._h = None
+
+    def alloc_prompt(self, seq_id, num_tokens, block_size=0):
+        """Returns (block size, slots)."""
+        np = self._np
+        slots = np.empty(max(num_tokens, 1), dtype=np.int64)
+        bs = np.zeros(1, dtype=np.int32)
+        _check(lib.pa_buddy_alloc_prompt(self._h, seq_id, num_tokens, block_size or 0, _i32p(bs),
+                                         _i64p(slots)), "pa_buddy_alloc_prompt")
+        return int(bs[0]), slots[:num_tokens]
+
+    def append_tokens(self, seq_id, n=1):
+        """Returns (slots, cow) with cow = (src, dst) or None."""
+        np = self._np
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        pair = np.empty(2, dtype=np.int32)
+        ncow = np.zeros(1, dtype=np.int32)
+        _check(lib.pa_buddy_append_tokens(self._h, seq_id, n, _i64p(slots), _i32p(pair),
+                                          _i32p(ncow)), "pa_buddy_append_tokens")
+        return slots[:n], ((int(pair[0]), int(pair[1])) if ncow[0] else None)
+
+    def append_tokens_batch(self, seq_ids, n=1):
+        """Returns (slots [B, n], cow_pairs [B, 2] (-1 = none), num_cow)."""
+        np = self._np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        B = ids.shape[0]
+        slots = np.empty((B, n), dtype=np.int64)
+        cow = np.empty((B, 2), dtype=np.int32)
+        ncow = np.zeros(1, dtype=np.int32)
+        _check(lib.pa_buddy_append_tokens_batch(self._h, _i64p(ids), B, n, _i64p(slots),
+                                                _i32p(cow), _i32p(ncow)),
+               "pa_buddy_append_tokens_batch")
+        return slots, cow, int(ncow[0])
+
+    def fork(self, parent_id, child_id):
+        _check(lib.pa_buddy_fork(self._h, parent_id, child_id), "pa_buddy_fork")
+
+    def free_seq(self, seq_id):
+        _check(lib.pa_buddy_free_seq(self._h, seq_id), "pa_buddy_free_seq")
+
+    def _table(self, seq_id):
+        np = self._np
+        n, ln, bs = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.pa_buddy_get_block_table(self._h, seq_id, None, 0, ctypes.byref(n),
+                                            ctypes.byref(ln), ctypes.byref(bs)),
+               "pa_buddy_get_block_table")
+        out = np.empty(max(n.value, 1), dtype=np.int32)
+        _check(lib.pa_buddy_get_block_table(self._h, seq_id, _i32p(out), n.value, None, None, None),
+               "pa_buddy_get_block_table")
+        return out[:n.value].tolist(), ln.value, bs.value
+
+    def block_table(self, seq_id):
+        return self._table(seq_id)[0]
+
+    def seq_len(self, seq_id):
+        return self._table(seq_id)[1]
+
+    def block_size(self, seq_id):
+        return self._table(seq_id)[2]
+
+    def pack(self, seq_ids, max_blocks):
+        """Tables [B, max_blocks] (-1 padded) and lengths [B] of sequences of one size."""
+        np = self._np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        t = np.empty((len(ids), max_blocks), dtype=np.int32)
+        ln = np.empty(len(ids), dtype=np.int32)
+        _check(lib.pa_buddy_pack_block_tables(self._h, _i64p(ids), len(ids), max_blocks, _i32p(t),
+                                              _i32p(ln)), "pa_buddy_pack_block_tables")
+        return t, ln
+
+    def free_tokens(self):
+        return int(lib.pa_buddy_free_tokens(self._h))
+
+    def free_list(self, block_size):
+        """Free blocks of one size, front first, as ids of that size's view."""
+        np = self._np
+        n = ctypes.c_int32()
+        _check(lib.pa_buddy_free_list(self._h, block_size, None, 0, ctypes.byref(n)),
+               "pa_buddy_free_list")
+        out = np.empty(max(n.value, 1), dtype=np.int32)
+        _check(lib.pa_buddy_free_list(self._h, block_size, _i32p(out), n.value, ctypes.byref(n)),
+               "pa_buddy_free_list")
+        return out[:n.value].tolist()
+
+    def refcount(self, block_size, block_id):
+        return int(lib.pa_buddy_block_refcount(self._h, block_size, block_id))
+
+
+class ArenaPool:
+    """One layer's K and V arena of arena_tokens rows per head, shared by
+    blocks of 8, 16, 32 and 64 tokens: view(b) is a PagedPool of block size
+    b over the same memory ([arena_tokens / b, heads, b, head_dim]).  fp8
+    arenas hold one scale array per view."""
+
+    def __init__(self, arena_tokens, num_heads, head_dim, kv_dtype, device, **flags):
+        tdt = torch.uint8 if kv_dtype == "fp8" else TORCH_DTYPE[kv_dtype]
+        self.k = torch.empty(arena_tokens * num_heads * head_dim, dtype=tdt, device=device)
+        self.v = torch.empty_like(self.k)
+        self.arena_tokens, self.num_heads, self.head_dim = arena_tokens, num_heads, head_dim
+        self.views = {}
+        for bs in BUDDY_SIZES:
+            shape = (arena_tokens // bs, num_heads, bs, head_dim)
+            ks = vs = None
+            if kv_dtype == "fp8":
+                ks = torch.ones(shape[:2], dtype=torch.float32, device=device)
+                vs = torch.ones(shape[:2], dtype=torch.float32, device=device)
+            self.views[bs] = PagedPool(self.k.view(shape), self.v.view(shape), ks, vs,
+                                       _NAME[kv_dtype], **flags)
+
+    def view(self, block_size):
+        return self.views[block_size]
 
 
 class PrefixIndex:

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libpa.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["status.cpp", "allocator.cpp", "prefix.cpp", "api.cpp", "cache_write.hip", "decode.hip",
+SOURCES = ["status.cpp", "allocator.cpp", "prefix.cpp", "buddy.cpp", "api.cpp", "cache_write.hip", "decode.hip",
            "prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

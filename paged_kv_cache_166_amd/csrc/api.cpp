@@ -24,8 +24,10 @@ pa_status check_pool(const char* fn, const pa_pool* p) {
     return fail(PA_ERR_INVALID, "%s: cache bases must be 128-byte aligned", fn);
   if (p->num_blocks <= 0 || p->num_heads <= 0 || p->num_heads > 65535)
     return fail(PA_ERR_INVALID, "%s: num_blocks=%d num_heads=%d", fn, p->num_blocks, p->num_heads);
-  if (p->block_size != 4 && p->block_size != 8 && p->block_size != 16 && p->block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (built: 4, 8, 16, 32)", fn, p->block_size);
+  if (p->block_size != 4 && p->block_size != 8 && p->block_size != 16 && p->block_size != 32 &&
+      p->block_size != 64)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (built: 4, 8, 16, 32, 64)", fn,
+                p->block_size);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", fn, p->head_dim);
   if (!valid_dtype(p->kv_dtype)) return fail(PA_ERR_INVALID, "%s: kv_dtype %d", fn, p->kv_dtype);

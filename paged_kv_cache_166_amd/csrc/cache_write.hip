@@ -116,11 +116,11 @@ __device__ __forceinline__ float wave_max(float v) {
 // earlier rows requantised if the scale grew, the run's rows stored, the
 // scale written -- K, then V (a window's runs one after another).  Runs of
 // different blocks touch disjoint tiles and scales, so no wave waits for
-// another.  Every step issues all its loads at once (a run is at most 32
-// rows of at most 128 elements: at most 8 chunks of 8 per lane), so a run
-// costs a few memory round trips, not one per row.
-constexpr int kMaxChunksPerLane = 8;   // 32 rows x 128 / 8 elements / 64 lanes
-
+// another.  Every step issues all its loads at once (a run is at most one
+// block of rows of at most 128 elements: kMaxChunksPerLane chunks of 8 per
+// lane, 8 for blocks up to 32 rows, 16 for 64), so a run costs a few memory
+// round trips, not one per row.
+template <int kMaxChunksPerLane>
 __device__ __forceinline__ void upkeep_one(const CacheWriteArgs& a, const void* in, uint8_t* tile,
                                            float* scale, int64_t t, int h, int p0, int n,
                                            int lane) {
@@ -171,6 +171,7 @@ __device__ __forceinline__ void upkeep_one(const CacheWriteArgs& a, const void* 
   if (lane == 0) *scale = s_new;
 }
 
+template <int kMaxChunksPerLane>
 __global__ __launch_bounds__(64) void reshape_fp8_upkeep_kernel(CacheWriteArgs a, int window) {
   const int64_t t0 = int64_t(blockIdx.x) * window;
   const int h = blockIdx.y;
@@ -194,11 +195,14 @@ __global__ __launch_bounds__(64) void reshape_fp8_upkeep_kernel(CacheWriteArgs a
     const int p0 = int(s % bs);
     // Run length in one round trip: lane i checks token t + i (i < bs - p0).
     const bool cont = lane < bs - p0 && t + lane < a.num_tokens && a.slots[t + lane] == s + lane;
-    const int n = int(__builtin_ctzll(~__ballot(cont)));   // leading run of ones
+    const uint64_t run = __ballot(cont);
+    const int n = run == ~uint64_t(0) ? 64 : int(__builtin_ctzll(~run));   // leading run of ones
     const int64_t si = blk * a.num_heads + h;
     const int64_t tile = si * bs * a.head_dim;
-    upkeep_one(a, a.key, (uint8_t*)a.k_cache + tile, a.k_scale + si, t, h, p0, n, lane);
-    upkeep_one(a, a.value, (uint8_t*)a.v_cache + tile, a.v_scale + si, t, h, p0, n, lane);
+    upkeep_one<kMaxChunksPerLane>(a, a.key, (uint8_t*)a.k_cache + tile, a.k_scale + si, t, h, p0,
+                                  n, lane);
+    upkeep_one<kMaxChunksPerLane>(a, a.value, (uint8_t*)a.v_cache + tile, a.v_scale + si, t, h,
+                                  p0, n, lane);
   }
 }
 
@@ -231,8 +235,12 @@ hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream)
     // wave runs them all at once.
     const int window = a.num_tokens > 1024 ? a.block_size : 1;
     const unsigned waves = unsigned((int64_t(a.num_tokens) + window - 1) / window);
-    hipLaunchKernelGGL(reshape_fp8_upkeep_kernel, dim3(waves, unsigned(a.num_heads)), dim3(64), 0,
-                       stream, a, window);
+    if (a.block_size * a.head_dim > 32 * 128)
+      hipLaunchKernelGGL(reshape_fp8_upkeep_kernel<16>, dim3(waves, unsigned(a.num_heads)),
+                         dim3(64), 0, stream, a, window);
+    else
+      hipLaunchKernelGGL(reshape_fp8_upkeep_kernel<8>, dim3(waves, unsigned(a.num_heads)),
+                         dim3(64), 0, stream, a, window);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0,

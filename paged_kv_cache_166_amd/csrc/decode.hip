@@ -54,7 +54,15 @@ struct Geo {
   static constexpr int kEpl = 16 / kElem;            // elements per lane per load
   static constexpr int kRows = 64 / kLpr;            // rows one wave-load covers
   static constexpr bool kIdleGroups = BS < kRows;    // groups past the block's rows
-  static constexpr int kLoads = kIdleGroups ? 1 : BS / kRows;
+  static constexpr int kTileLoads = kIdleGroups ? 1 : BS / kRows;  // wave-loads per tile
+  // A tile is consumed in sub-tiles of at most 8 wave-loads (two buffers of
+  // K and V within 128 registers), 4 for 64-row blocks: those run like
+  // 16-row blocks of 16-bit elements, with a quarter of the table lookups.
+  static constexpr int kMaxLoads = BS >= 64 ? 4 : 8;
+  static constexpr int kLoads = kTileLoads < kMaxLoads ? kTileLoads : kMaxLoads;
+  static constexpr int kSubs = kTileLoads / kLoads;
+  static constexpr int kSubRows = kIdleGroups ? BS : kLoads * kRows;
+  static constexpr int64_t kSubBytes = int64_t(kSubRows) * kRowBytes;
   static constexpr int64_t kTileBytes = int64_t(BS) * kRowBytes;
   static_assert(kLpr >= 4 && kLpr <= 32, "row must span 4..32 lanes");
 };
@@ -227,7 +235,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   // This wave's blocks are wave, wave + NW, ... of the partition (n_w <= 64
   // of them); lane t of `tab` holds the block id of the wave's t-th block.
+  // Its work units are their sub-tiles in order: unit u is sub-tile
+  // u % kSubs of its (u / kSubs)-th block.
   const int n_w = wave < nb ? (nb - wave + NW - 1) / NW : 0;
+  const int n_u = n_w * G::kSubs;
   const int64_t blk_stride = int64_t(H) * G::kTileBytes;
   const char* kbase = (const char*)a.k_cache + int64_t(head) * G::kTileBytes + lane * 16;
   const char* vbase = (const char*)a.v_cache + int64_t(head) * G::kTileBytes + lane * 16;
@@ -240,15 +251,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   uint4 k0[G::kLoads], v0[G::kLoads], k1[G::kLoads], v1[G::kLoads];
   int p0 = 0, p1 = 0;
 
-  // Loads of the wave's j-th block.  Past its last block (the pipeline's
+  // Loads of the wave's unit u.  Past its last unit (the pipeline's
   // prefetch after the final one, never consumed) both K and V re-read the
-  // last block's K tile: K loads are ordinary ones, so that tile is still in
-  // the L2, whereas a streamed V tile would come from HBM again.
-  auto issue = [&](uint4* kr, uint4* vr, int& phys, int j) {
-    const bool past = j >= n_w;
-    phys = __builtin_amdgcn_readlane(tab, past ? n_w - 1 : j);
-    const char* kp = kbase + int64_t(phys) * blk_stride;
-    const char* vp = past ? kp : vbase + int64_t(phys) * blk_stride;
+  // last unit's K sub-tile: K loads are ordinary ones, so it is still in the
+  // L2, whereas a streamed V sub-tile would come from HBM again.
+  auto issue = [&](uint4* kr, uint4* vr, int& phys, int u) {
+    const bool past = u >= n_u;
+    const int ue = past ? n_u - 1 : u;
+    phys = __builtin_amdgcn_readlane(tab, ue / G::kSubs);
+    const int64_t sub = int64_t(ue % G::kSubs) * G::kSubBytes;
+    const char* kp = kbase + int64_t(phys) * blk_stride + sub;
+    const char* vp = past ? kp : vbase + int64_t(phys) * blk_stride + sub;
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       if (row_ok) {
@@ -266,15 +279,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  auto consume = [&](uint4* kr, uint4* vr, int phys, int jl) {
+  auto consume = [&](uint4* kr, uint4* vr, int phys, int u) {
     float mul_k = a.scale_log2;
     float mul_v = 1.f;
     if constexpr (KV == PA_FP8_E4M3) {
       mul_k *= a.k_scale[int64_t(phys) * H + head];
       mul_v = a.v_scale[int64_t(phys) * H + head];
     }
-    const int tok0 = (blk0 + jl) * BS + grp;  // token of load 0 in this lane's group
-    const bool full = (blk0 + jl + 1) * BS <= L;
+    const int jl = wave + (u / G::kSubs) * NW;  // block of the partition
+    const int r0 = (blk0 + jl) * BS + (u % G::kSubs) * G::kSubRows;  // first token of the unit
+    const int tok0 = r0 + grp;                    // token of load 0 in this lane's group
+    const bool full = r0 + G::kSubRows <= L;
     float s[G::kLoads];
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
@@ -309,17 +324,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     m = mx;
   };
 
-  // Two-deep software pipeline over this wave's n_w blocks (the prefetch
+  // Two-deep software pipeline over this wave's n_u units (the prefetch
   // after the last one is a dummy, see issue()).
-  if (n_w > 0) {
+  if (n_u > 0) {
     issue(k0, v0, p0, 0);
     for (int i = 0;;) {
       issue(k1, v1, p1, i + 1);
-      consume(k0, v0, p0, wave + i * NW);
-      if (++i >= n_w) break;
+      consume(k0, v0, p0, i);
+      if (++i >= n_u) break;
       issue(k0, v0, p0, i + 1);
-      consume(k1, v1, p1, wave + i * NW);
-      if (++i >= n_w) break;
+      consume(k1, v1, p1, i);
+      if (++i >= n_u) break;
     }
   }
 
@@ -463,6 +478,7 @@ hipError_t launch_bs(const DecodeArgs& a, int bs, bool sv, int num_seqs, hipStre
     case 8: return launch_t<KV, D, 8>(a, sv, num_seqs, stream);
     case 16: return launch_t<KV, D, 16>(a, sv, num_seqs, stream);
     case 32: return launch_t<KV, D, 32>(a, sv, num_seqs, stream);
+    case 64: return launch_t<KV, D, 64>(a, sv, num_seqs, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -278,9 +278,10 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   const uint16_t* kpool = (const uint16_t*)a.k_cache;
   const uint16_t* vpool = (const uint16_t*)a.v_cache;
 
-  // Inside a tile a lane always loads the same row-in-block and chunk (tiles
-  // start at multiples of the block size), so its byte offset from the
-  // (block, head) base is fixed: only the block id changes from tile to tile.
+  // Inside a tile a lane always loads the same row-in-tile and chunk, so its
+  // byte offset from the (block, head) base is fixed: only the block id
+  // changes from tile to tile -- and, for blocks longer than a tile, which
+  // part of the block the tile is (a uniform offset).
   uint32_t off_k[kLoadsPerWave], off_v[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
@@ -298,12 +299,13 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     const int kb = t * kBN;
     if (kBlocksPerLoad == 1 && kb + kBN <= L) {
       // Whole tile inside the sequence: one block per wave-load, uniform base.
+      const int64_t in_blk = BS > kBN ? int64_t(kb % BS) * kRowBytes : 0;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int li = wave * kLoadsPerWave + i;
         const int64_t blk = table[__builtin_amdgcn_readfirstlane((kb + li * kRowsPerLoad) / BS)];
-        load_lds16(kbase0 + blk * tile_stride + off_k[i], dk + li * 1024);
-        load_lds16(vbase0 + blk * tile_stride + off_v[i], dv + li * 1024);
+        load_lds16(kbase0 + blk * tile_stride + in_blk + off_k[i], dk + li * 1024);
+        load_lds16(vbase0 + blk * tile_stride + in_blk + off_v[i], dv + li * 1024);
       }
       return;
     }
@@ -548,6 +550,7 @@ hipError_t launch_bs(const PrefillArgs& a, int bs, int mq, hipStream_t stream) {
     case 8: return launch_t<KV, D, 8>(a, mq, stream);
     case 16: return launch_t<KV, D, 16>(a, mq, stream);
     case 32: return launch_t<KV, D, 32>(a, mq, stream);
+    case 64: return launch_t<KV, D, 64>(a, mq, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("kv", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("bs", [4, 16, 32])
+@pytest.mark.parametrize("bs", [4, 16, 32, 64])
 def test_reshape_and_cache_bit_exact(kv, D, bs):
     sc = Scenario(24, 3, bs, D, kv, seed=11)
     rng = np.random.default_rng(12)
@@ -32,7 +32,7 @@ def test_reshape_and_cache_bit_exact(kv, D, bs):
 
 @pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("bs", [8, 32, 64])
 def test_reshape_and_cache_fp8_bit_exact(in_dtype, D, bs):
     """Codes are RNE-saturate(x / scale) with the division in float32; the
     scales are chosen so that some values saturate and some are subnormal."""

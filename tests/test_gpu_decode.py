@@ -65,7 +65,7 @@ def test_tiny_decode_workload():
 
 @pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "fp8"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("bs", [4, 8, 16, 32])
+@pytest.mark.parametrize("bs", [4, 8, 16, 32, 64])
 def test_decode_sweep(kv, D, bs):
     """Ragged lengths (0, 1, around the block size, several partitions) on a
     shuffled pool whose unused bytes are NaN; automatic and forced split-K."""

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("D,bs", [(128, 16), (64, 4), (128, 32)])
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 4), (128, 32), (128, 64), (64, 64)])
 def test_appends_grow_keep_and_shrink(in_dtype, D, bs):
     H = 3
     # stale scales (50..100) in every block: a run that starts a block must ignore them
@@ -35,8 +35,9 @@ def test_appends_grow_keep_and_shrink(in_dtype, D, bs):
 
 
 @pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
-def test_chunks_requantise_the_partly_filled_block(in_dtype):
-    H, D, bs = 4, 128, 32
+@pytest.mark.parametrize("bs", [32, 64])
+def test_chunks_requantise_the_partly_filled_block(in_dtype, bs):
+    H, D = 4, 128
     sc = Scenario(200, H, bs, D, "fp8", seed=77, in_dtype=in_dtype, fp8_auto_scale=True)
     rng = np.random.default_rng(77)
     for i, (L, a) in enumerate([(10, 0.5), (40, 2.0), (33, 1.0), (64, 0.01)]):

@@ -36,7 +36,7 @@ def _run(sc, seqs, qsl, q_dev, scale, out_dtype=torch.float32):
 
 @pytest.mark.parametrize("kv", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("bs", [4, 16, 32])
+@pytest.mark.parametrize("bs", [4, 16, 32, 64])
 def test_prefill_sweep(kv, D, bs):
     """Context 0 / short / ragged, chunks of 1 .. 200 rows (partial query
     tiles), a shuffled NaN-filled pool."""
