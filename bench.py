@@ -300,6 +300,108 @@ class DecodeBench:
         res["bytes"] = nbytes
         return res
 
+    def block_sizes(self, reps=20):
+        """pa_decode of the batch at its current lengths with other block
+        sizes: one pool per fixed size (8, 16, 32, 64; same shuffled-pool
+        construction), and one arena whose sequences take the size the size
+        rule gives their length (one pa_decode per size, back to back on the
+        stream, timed as one).  Event-timed medians, warm caches; bytes =
+        this launch's algorithmic bytes (K/V rows, q, out; tables at each
+        size).  Memory: tokens reserved (whole blocks) against tokens held."""
+        lens = self.lens_now()
+        H, D, B = self.H, self.D, self.B
+        row = H * D * ELEM[self.kv]
+        tokens = int(np.sum(lens))
+        g = torch.Generator(device=self.device)
+        g.manual_seed(7)
+        tdt = pa.TORCH_DTYPE[self.qdt]
+        q = torch.randn((B, H, D), generator=g, device=self.device).to(tdt)
+
+        def fill(*ts):
+            for t in ts:
+                for i in range(0, t.shape[0], 1024):
+                    x = torch.randn((min(1024, t.shape[0] - i),) + tuple(t.shape[1:]), generator=g,
+                                    device=self.device)
+                    t[i:i + x.shape[0]] = x.to(t.dtype)
+
+        def timed(calls):
+            ts = []
+            for r in range(reps + 3):
+                tm = Timer()
+                tm.start()
+                for c in calls:
+                    c()
+                tm.stop()
+                torch.cuda.synchronize()
+                if r >= 3:
+                    ts.append(tm.seconds())
+            return float(np.median(ts))
+
+        def nbytes(groups):
+            b = 2 * tokens * row + B * H * D * ELEM[self.qdt] * 2 + B * 4
+            return b + sum(int(np.sum(-(-ln // bs))) * 4 for bs, ln in groups)
+
+        res = {"tokens": tokens, "fixed": {}}
+        for bs in (8, 16, 32, 64):
+            N = int(np.sum(-(-lens // bs))) + 64
+            alloc = pa.Allocator(N, bs, W.free_order(self.cfg["seed"] + bs, N))
+            for i in range(B):
+                alloc.alloc_prompt(i, int(lens[i]))
+            pool = pa.PagedPool.empty(N, H, bs, D, self.kv, self.device, stream_kv=self.stream_kv)
+            fill(pool.k_cache, pool.v_cache)
+            maxb = int(np.max(-(-lens // bs)))
+            t, ln = alloc.pack(self.ids, maxb)
+            td, lnd = torch.from_numpy(t).to(self.device), torch.from_numpy(ln).to(self.device)
+            out = torch.empty_like(q)
+            ws = pa.decode_workspace(pool, B, maxb, 0)
+            sec = timed([lambda: pa.pa_decode(out, q, pool, td, lnd, self.scale, 0, ws)])
+            nb = nbytes([(bs, lens)])
+            res["fixed"][bs] = {"us": sec * 1e6, "GBps": nb / sec / 1e9,
+                                "reserved_tokens": int(np.sum(-(-lens // bs) * bs))}
+            del pool, alloc
+        arena_tokens = -(-int(np.sum(-(-lens // 64) * 64)) // 64) * 64 + 64 * 64
+        ba = pa.BuddyAllocator(arena_tokens, W.free_order(self.cfg["seed"], arena_tokens // 64))
+        sizes = np.array([ba.alloc_prompt(i, int(lens[i]))[0] for i in range(B)])
+        arena = pa.ArenaPool(arena_tokens, H, D, self.kv, self.device, stream_kv=self.stream_kv)
+        fill(arena.k, arena.v)
+        calls, groups, keep = [], [], []
+        mpools, mtabs, mbegin, mrows = [], [], [0], []
+        for bs in sorted(set(sizes.tolist())):
+            idx = np.nonzero(sizes == bs)[0]
+            ids = self.ids[idx]
+            maxb = int(np.max(-(-lens[idx] // bs)))
+            t, ln = ba.pack(ids, maxb)
+            td, lnd = torch.from_numpy(t).to(self.device), torch.from_numpy(ln).to(self.device)
+            qg = q[torch.from_numpy(idx).to(self.device)].contiguous()
+            og = torch.empty_like(qg)
+            view = arena.view(bs)
+            ws = pa.decode_workspace(view, len(ids), maxb, 0)
+            keep.append((td, lnd, qg, og, ws))
+            calls.append(lambda v=view, qg=qg, og=og, td=td, lnd=lnd, ws=ws:
+                         pa.pa_decode(og, qg, v, td, lnd, self.scale, 0, ws))
+            groups.append((bs, lens[idx]))
+            mpools.append(view)
+            mtabs.append(td)
+            mbegin.append(mbegin[-1] + len(ids))
+            mrows.append(idx)
+        sec = timed(calls)
+        # the same batch in one pa_decode_multi launch (rows grouped by size)
+        rows = torch.from_numpy(np.concatenate(mrows)).to(self.device)
+        qm = q[rows].contiguous()
+        om = torch.empty_like(qm)
+        lm = torch.from_numpy(lens[np.concatenate(mrows)].astype(np.int32)).to(self.device)
+        wsm = pa.decode_multi_workspace(mpools, [t.shape[1] for t in mtabs], B, 0)
+        sec_m = timed([lambda: pa.pa_decode_multi(om, qm, mpools, mtabs, lm, mbegin, self.scale, 0,
+                                                  wsm)])
+        res["by_length"] = {"us": sec_m * 1e6, "GBps": nbytes(groups) / sec_m / 1e9,
+                            "launch": "pa_decode_multi (one launch)",
+                            "us_one_launch_per_size": sec * 1e6, "sizes": len(calls),
+                            "sequences_per_size": {int(b): int(np.sum(sizes == b)) for b in set(sizes.tolist())},
+                            "reserved_tokens": int(sum(int(np.sum(-(-ln // bs) * bs)) for bs, ln in groups))}
+        del arena, ba, keep, qm, om, wsm
+        torch.cuda.empty_cache()
+        return res
+
     def cold_series(self, reps=10, flush_mib=512):
         """pa_decode on the middle layer with the caches cold: a read of
         flush_mib MiB (twice the 256 MB Infinity Cache) before each timed
@@ -758,6 +860,9 @@ def main():
         res["pa_decode_us_per_layer"] = kt * 1e6
         log("bench: cold-cache series")
         res["cold"] = b.cold_series()
+        if args.workload == "llama13b_decode":
+            log("bench: block sizes")
+            res["block_sizes"] = b.block_sizes()
         if args.workload == "long_fp8_decode":
             res["fp8_write"] = b.fp8_write_series()
         if args.workload == "prefix_cow":

@@ -180,6 +180,37 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_multi -- pa_decode of one batch whose sequences live in several
+ * pools with the same num_heads, head_dim and kv_dtype (typically the
+ * block-size views of one arena, pa_buddy_*), in one launch (plus the merge
+ * launch when a sequence spans more than one partition).  Rows of out, q and
+ * context_lens are grouped by pool: group g is rows [seq_begin[g],
+ * seq_begin[g+1]) and uses pools[g] and block_tables[g].
+ *   pools           host, [num_groups] (1..8).
+ *   block_tables    host array of num_groups device pointers; group g's
+ *                   tables are [rows of g][max_blocks_per_seq[g]] int32 in
+ *                   pools[g]'s block ids (may be NULL for an empty group).
+ *   max_blocks_per_seq  host, [num_groups], each >= 1.
+ *   seq_begin       host, [num_groups + 1], non-decreasing, seq_begin[0] = 0;
+ *                   seq_begin[num_groups] is the batch size.
+ *   partition_tokens  tokens per split-K partition in every group (0: 512);
+ *                   a multiple of every group's block size, at most 256
+ *                   blocks of each.
+ *   workspace       >= pa_decode_multi_workspace_bytes(...) bytes.
+ * The V loads stream past the caches only if every pool has
+ * PA_POOL_STREAM_KV.  Other arguments and errors as pa_decode.
+ */
+size_t pa_decode_multi_workspace_bytes(const pa_pool* pools, const int32_t* max_blocks_per_seq,
+                                       int32_t num_groups, int32_t num_seqs,
+                                       int32_t partition_tokens);
+pa_status pa_decode_multi(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                          const pa_pool* pools, int32_t num_groups,
+                          const int32_t* const* block_tables, const int32_t* max_blocks_per_seq,
+                          const int32_t* seq_begin, const int32_t* context_lens, float scale,
+                          int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
  * pa_prefill_chunk -- causal attention of a chunk of query tokens against the
  * sequence's paged context (blog article section 3.2.2 forward pass with its
  * causal mask; the mask is aligned so that the chunk's rows are the last

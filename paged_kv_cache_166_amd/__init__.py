@@ -38,6 +38,7 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
 EXPORTS = [
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_auto_partition_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_chunk",
+    "pa_decode_multi_workspace_bytes", "pa_decode_multi",
     "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_prompt", "pa_append_tokens",
     "pa_append_tokens_batch", "pa_fork", "pa_free_seq", "pa_get_block_table",
     "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
@@ -77,6 +78,9 @@ def _load():
         "pa_decode_auto_partition_blocks": (I32, [P, I32, I32]),
         "pa_decode_workspace_bytes": (SZ, [P, I32, I32, I32]),
         "pa_decode": (I32, [VP, I32, VP, I32, P, VP, I32, VP, I32, ctypes.c_float, I32, VP, SZ, VP]),
+        "pa_decode_multi_workspace_bytes": (SZ, [P, pi32, I32, I32, I32]),
+        "pa_decode_multi": (I32, [VP, I32, VP, I32, P, I32, VP, pi32, pi32, VP, ctypes.c_float, I32,
+                                  VP, SZ, VP]),
         "pa_prefill_chunk": (I32, [VP, I32, VP, I32, P, VP, I32, VP, VP, I32, I32, ctypes.c_float,
                                    VP]),
         "pa_allocator_create": (I32, [I32, I32, pi32, ctypes.POINTER(VP)]),
@@ -290,6 +294,42 @@ def pa_prefill_chunk(out, q, pool, block_tables, context_lens, query_start_loc, 
                                 _ptr(block_tables), maxb, _ptr(context_lens),
                                 _ptr(query_start_loc), B, int(max_query_len), float(scale),
                                 _stream(stream, pool.device)), "pa_prefill_chunk")
+
+
+def _pool_array(pools):
+    arr = (_Pool * len(pools))(*[p._struct for p in pools])
+    return arr, ctypes.cast(arr, ctypes.POINTER(_Pool))
+
+
+def decode_multi_workspace(pools, max_blocks_per_seq, num_seqs, partition_tokens=0):
+    """A workspace tensor for pa_decode_multi (or None if none is needed)."""
+    _, parr = _pool_array(pools)
+    mb = (ctypes.c_int32 * len(pools))(*[int(x) for x in max_blocks_per_seq])
+    n = lib.pa_decode_multi_workspace_bytes(parr, mb, len(pools), num_seqs, partition_tokens)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=pools[0].device)
+
+
+def pa_decode_multi(out, q, pools, block_tables, context_lens, seq_begin, scale,
+                    partition_tokens=0, workspace=None, stream=None):
+    """One decode launch over several pools: rows [seq_begin[g], seq_begin[g+1])
+    of out/q/context_lens use pools[g] and block_tables[g] ([rows, max_blocks_g]
+    int32 on the device, or None for an empty group)."""
+    assert len(pools) == len(block_tables) and len(seq_begin) == len(pools) + 1
+    assert q.is_contiguous() and out.is_contiguous() and context_lens.dtype == torch.int32
+    arr, parr = _pool_array(pools)
+    G = len(pools)
+    tabs = (ctypes.c_void_p * G)(*[t.data_ptr() if t is not None else 0 for t in block_tables])
+    for t in block_tables:
+        assert t is None or (t.dtype == torch.int32 and t.is_contiguous() and t.dim() == 2)
+    mb = (ctypes.c_int32 * G)(*[t.shape[1] if t is not None else 1 for t in block_tables])
+    sb = (ctypes.c_int32 * (G + 1))(*[int(x) for x in seq_begin])
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib.pa_decode_multi(_ptr(out), dtype_code(out), _ptr(q), dtype_code(q), parr, G,
+                               ctypes.cast(tabs, ctypes.c_void_p), mb, sb, _ptr(context_lens),
+                               float(scale), int(partition_tokens), _ptr(workspace), ws_bytes,
+                               _stream(stream, pools[0].device)), "pa_decode_multi")
 
 
 # ------------------------------------------------------------ host allocator

@@ -2,6 +2,7 @@
 // Nothing is launched when a check fails.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "kernels.h"
@@ -59,9 +60,9 @@ struct WsLayout {
   int32_t parts;
 };
 
-WsLayout ws_layout(const pa_pool* p, int32_t num_seqs, int32_t max_blocks, int32_t part_blocks) {
+WsLayout ws_layout_parts(const pa_pool* p, int32_t num_seqs, int32_t parts) {
   WsLayout w{};
-  w.parts = (max_blocks + part_blocks - 1) / part_blocks;
+  w.parts = parts;
   if (w.parts <= 1) return w;
   const int64_t sh = int64_t(num_seqs) * p->num_heads;
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
@@ -69,6 +70,35 @@ WsLayout ws_layout(const pa_pool* p, int32_t num_seqs, int32_t max_blocks, int32
   w.acc_off = up(sh * w.parts * 2 * 4);
   w.bytes = w.acc_off + up(sh * w.parts * p->head_dim * 4);
   return w;
+}
+
+WsLayout ws_layout(const pa_pool* p, int32_t num_seqs, int32_t max_blocks, int32_t part_blocks) {
+  return ws_layout_parts(p, num_seqs, (max_blocks + part_blocks - 1) / part_blocks);
+}
+
+// The several-pool decode: pools agree on heads, head_dim, KV type; every
+// group's block size divides the partition length; partitions per sequence
+// at most ceil(max_blocks * block_size / part_tokens) over the groups.
+pa_status check_multi(const char* fn, const pa_pool* pools, int32_t num_groups,
+                      const int32_t* max_blocks, int32_t part_tokens, int32_t* parts) {
+  if (!pools || !max_blocks || num_groups < 1 || num_groups > pa::kMaxDecodeGroups)
+    return fail(PA_ERR_INVALID, "%s: 1..%d groups with pools and table widths", fn,
+                pa::kMaxDecodeGroups);
+  *parts = 1;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    if (pa_status st = check_pool(fn, &pools[g])) return st;
+    if (pools[g].num_heads != pools[0].num_heads || pools[g].head_dim != pools[0].head_dim ||
+        pools[g].kv_dtype != pools[0].kv_dtype)
+      return fail(PA_ERR_INVALID, "%s: pools differ in heads, head_dim or KV type", fn);
+    const int32_t bs = pools[g].block_size;
+    if (part_tokens % bs != 0 || part_tokens / bs > 256)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "%s: partition of %d tokens is not 1..256 blocks of %d", fn, part_tokens, bs);
+    if (max_blocks[g] <= 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq <= 0", fn);
+    const int64_t p = (int64_t(max_blocks[g]) * bs + part_tokens - 1) / part_tokens;
+    *parts = std::max<int32_t>(*parts, int32_t(p));
+  }
+  return PA_OK;
 }
 
 }  // namespace
@@ -189,6 +219,90 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
   return hip_status(fn, pa::launch_decode(a, pool->kv_dtype, pool->head_dim, pool->block_size,
                                           (pool->flags & PA_POOL_STREAM_KV) != 0, num_seqs,
                                           stream));
+}
+
+size_t pa_decode_multi_workspace_bytes(const pa_pool* pools, const int32_t* max_blocks_per_seq,
+                                       int32_t num_groups, int32_t num_seqs,
+                                       int32_t partition_tokens) {
+  const int32_t pt = partition_tokens > 0 ? partition_tokens : 512;
+  int32_t parts = 1;
+  if (num_seqs <= 0 ||
+      check_multi("pa_decode_multi_workspace_bytes", pools, num_groups, max_blocks_per_seq, pt,
+                  &parts))
+    return 0;
+  return size_t(ws_layout_parts(&pools[0], num_seqs, parts).bytes);
+}
+
+pa_status pa_decode_multi(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                          const pa_pool* pools, int32_t num_groups,
+                          const int32_t* const* block_tables, const int32_t* max_blocks_per_seq,
+                          const int32_t* seq_begin, const int32_t* context_lens, float scale,
+                          int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  const char* fn = "pa_decode_multi";
+  const int32_t pt = partition_tokens > 0 ? partition_tokens : 512;
+  if (partition_tokens < 0) return fail(PA_ERR_INVALID, "%s: partition_tokens < 0", fn);
+  int32_t parts = 1;
+  if (pa_status st = check_multi(fn, pools, num_groups, max_blocks_per_seq, pt, &parts)) return st;
+  if (!seq_begin || !block_tables) return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (seq_begin[0] != 0) return fail(PA_ERR_INVALID, "%s: seq_begin[0] must be 0", fn);
+  for (int32_t g = 0; g < num_groups; ++g) {
+    if (seq_begin[g + 1] < seq_begin[g])
+      return fail(PA_ERR_INVALID, "%s: seq_begin must not decrease", fn);
+    if (seq_begin[g + 1] > seq_begin[g] && !block_tables[g])
+      return fail(PA_ERR_INVALID, "%s: group %d has sequences but no table", fn, g);
+  }
+  const int32_t num_seqs = seq_begin[num_groups];
+  if (num_seqs > 65535) return fail(PA_ERR_INVALID, "%s: num_seqs %d", fn, num_seqs);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !context_lens) return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(q, 16) || !aligned(out, 16))
+    return fail(PA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
+  const pa_pool* p0 = &pools[0];
+  if (p0->kv_dtype == PA_FP8_E4M3) {
+    if (!valid_io_dtype(q_dtype)) return fail(PA_ERR_INVALID, "%s: q_dtype %d", fn, q_dtype);
+  } else if (q_dtype != p0->kv_dtype) {
+    return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype %d must equal kv_dtype %d", fn, q_dtype,
+                p0->kv_dtype);
+  }
+  if (out_dtype != PA_F32 && out_dtype != q_dtype)
+    return fail(PA_ERR_INVALID, "%s: out_dtype must be f32 or q_dtype", fn);
+  const WsLayout w = ws_layout_parts(p0, num_seqs, parts);
+  if (w.parts > 1) {
+    if (!workspace || size_t(w.bytes) > workspace_bytes || !aligned(workspace, 256))
+      return fail(PA_ERR_INVALID, "%s: workspace of %lld bytes, 256-byte aligned, is required",
+                  fn, (long long)w.bytes);
+  }
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeMultiArgs m{};
+  pa::DecodeArgs& a = m.base;
+  a.out = out;
+  a.q = q;
+  a.context_lens = context_lens;
+  a.ws_ml = w.parts > 1 ? reinterpret_cast<float*>(ws + w.ml_off) : nullptr;
+  a.ws_acc = w.parts > 1 ? reinterpret_cast<float*>(ws + w.acc_off) : nullptr;
+  a.num_heads = p0->num_heads;
+  a.max_parts = w.parts < 1 ? 1 : w.parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.q_dtype = q_dtype;
+  a.out_dtype = out_dtype;
+  m.num_groups = num_groups;
+  m.part_tokens = pt;
+  bool stream_v = true;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    pa::DecodeGroup& d = m.g[g];
+    d.k_cache = pools[g].k_cache;
+    d.v_cache = pools[g].v_cache;
+    d.k_scale = pools[g].k_scale;
+    d.v_scale = pools[g].v_scale;
+    d.block_tables = block_tables[g];
+    d.max_blocks_per_seq = max_blocks_per_seq[g];
+    d.block_size = pools[g].block_size;
+    d.seq_begin = seq_begin[g];
+    stream_v = stream_v && (pools[g].flags & PA_POOL_STREAM_KV) != 0;
+  }
+  return hip_status(fn, pa::launch_decode_multi(m, p0->kv_dtype, p0->head_dim, stream_v,
+                                                num_seqs, stream));
 }
 
 pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,

@@ -46,7 +46,8 @@
 namespace pa {
 namespace {
 
-template <int KV, int D, int BS>
+// MaxL: wave-loads per sub-tile at most (see kLoads).
+template <int KV, int D, int BS, int MaxL>
 struct Geo {
   static constexpr int kElem = dtype_bytes(KV);
   static constexpr int kRowBytes = D * kElem;
@@ -55,11 +56,12 @@ struct Geo {
   static constexpr int kRows = 64 / kLpr;            // rows one wave-load covers
   static constexpr bool kIdleGroups = BS < kRows;    // groups past the block's rows
   static constexpr int kTileLoads = kIdleGroups ? 1 : BS / kRows;  // wave-loads per tile
-  // A tile is consumed in sub-tiles of at most 8 wave-loads (two buffers of
-  // K and V within 128 registers), 4 for 64-row blocks: those run like
-  // 16-row blocks of 16-bit elements, with a quarter of the table lookups.
-  static constexpr int kMaxLoads = BS >= 64 ? 4 : 8;
-  static constexpr int kLoads = kTileLoads < kMaxLoads ? kTileLoads : kMaxLoads;
+  // A tile is consumed in sub-tiles of at most MaxL wave-loads: 8 (two
+  // buffers of K and V within 128 registers), 4 for 64-row blocks, which
+  // then run like 16-row blocks of 16-bit elements with a quarter of the
+  // table lookups (and 4 for every size in the several-pool kernel, whose
+  // register budget is that of its largest branch).
+  static constexpr int kLoads = kTileLoads < MaxL ? kTileLoads : MaxL;
   static constexpr int kSubs = kTileLoads / kLoads;
   static constexpr int kSubRows = kIdleGroups ? BS : kLoads * kRows;
   static constexpr int64_t kSubBytes = int64_t(kSubRows) * kRowBytes;
@@ -188,9 +190,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr int kMaxPartBlocks = 256;
 
-template <int KV, int D, int BS, int NW, bool kStreamV>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  using G = Geo<KV, D, BS>;
+constexpr int default_max_loads(int bs) { return bs >= 64 ? 4 : 8; }
+
+// One workgroup's work: (head, sequence, partition) = blockIdx (x, y, z).
+template <int KV, int D, int BS, int NW, bool kStreamV, int MaxL>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
+  using G = Geo<KV, D, BS, MaxL>;
   using Ops = KvOps<KV>;
   constexpr int E = G::kEpl;
   static_assert(E == Ops::kEpl, "lane element count");
@@ -391,6 +396,44 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
+template <int KV, int D, int BS, int NW, bool kStreamV>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+  decode_body<KV, D, BS, NW, kStreamV, default_max_loads(BS)>(a);
+}
+
+// A batch over several pools (same heads, head_dim and KV type; e.g. the
+// block-size views of one arena): the sequences of group g are rows
+// [seq_begin, next group's seq_begin) of the batch and use group g's pool
+// and block table.  Each workgroup finds its group (a uniform scan of at most
+// kMaxGroups entries), then runs the body of its group's block size with
+// sub-tiles of at most 4 wave-loads, so that every branch fits the same
+// register budget.  Partitions are part_tokens long in every group.
+template <int KV, int D, int NW, bool kStreamV>
+__global__ __launch_bounds__(NW * 64) void decode_multi_kernel(DecodeMultiArgs m) {
+  const int seq = blockIdx.y;
+  int g = 0;
+  for (int i = 1; i < m.num_groups; ++i)
+    if (seq >= m.g[i].seq_begin) g = i;
+  const DecodeGroup& grp = m.g[g];
+  DecodeArgs a = m.base;
+  a.k_cache = grp.k_cache;
+  a.v_cache = grp.v_cache;
+  a.k_scale = grp.k_scale;
+  a.v_scale = grp.v_scale;
+  // the body indexes rows by the batch-wide sequence number
+  a.block_tables = grp.block_tables - int64_t(grp.seq_begin) * grp.max_blocks_per_seq;
+  a.max_blocks_per_seq = grp.max_blocks_per_seq;
+  a.block_size = grp.block_size;
+  a.part_blocks = m.part_tokens / grp.block_size;
+  switch (grp.block_size) {
+    case 4: decode_body<KV, D, 4, NW, kStreamV, 4>(a); break;
+    case 8: decode_body<KV, D, 8, NW, kStreamV, 4>(a); break;
+    case 16: decode_body<KV, D, 16, NW, kStreamV, 4>(a); break;
+    case 32: decode_body<KV, D, 32, NW, kStreamV, 4>(a); break;
+    case 64: decode_body<KV, D, 64, NW, kStreamV, 4>(a); break;
+  }
+}
+
 // Merge the partitions of each (sequence, head) that has more than one:
 // M = max_p m_p, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
 // R threads per output element take every R-th partition with a running
@@ -491,7 +534,49 @@ hipError_t launch_d(const DecodeArgs& a, int d, int bs, bool sv, int num_seqs,
   return hipErrorInvalidValue;
 }
 
+template <int KV, int D>
+hipError_t launch_multi_t(const DecodeMultiArgs& m, bool stream_v, int num_seqs,
+                          hipStream_t stream) {
+  dim3 grid(m.base.num_heads, num_seqs, m.base.max_parts);
+  if (stream_v)
+    hipLaunchKernelGGL((decode_multi_kernel<KV, D, kWaves, true>), grid, dim3(kWaves * 64), 0,
+                       stream, m);
+  else
+    hipLaunchKernelGGL((decode_multi_kernel<KV, D, kWaves, false>), grid, dim3(kWaves * 64), 0,
+                       stream, m);
+  if (m.base.max_parts > 1) {
+    // The merge kernel counts a sequence's partitions as ceil(L / block_size
+    // / part_blocks): in tokens, with block_size 1.
+    DecodeArgs a = m.base;
+    a.block_size = 1;
+    a.part_blocks = m.part_tokens;
+    constexpr int R = 512 / D;
+    hipLaunchKernelGGL((decode_merge_kernel<D, R>), dim3(a.num_heads, num_seqs), dim3(D * R), 0,
+                       stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <int KV>
+hipError_t launch_multi_d(const DecodeMultiArgs& m, int d, bool sv, int num_seqs,
+                          hipStream_t stream) {
+  if (d == 64) return launch_multi_t<KV, 64>(m, sv, num_seqs, stream);
+  if (d == 128) return launch_multi_t<KV, 128>(m, sv, num_seqs, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_decode_multi(const DecodeMultiArgs& m, int kv_dtype, int head_dim,
+                               bool stream_v, int num_seqs, hipStream_t stream) {
+  switch (kv_dtype) {
+    case PA_F32: return launch_multi_d<PA_F32>(m, head_dim, stream_v, num_seqs, stream);
+    case PA_F16: return launch_multi_d<PA_F16>(m, head_dim, stream_v, num_seqs, stream);
+    case PA_BF16: return launch_multi_d<PA_BF16>(m, head_dim, stream_v, num_seqs, stream);
+    case PA_FP8_E4M3: return launch_multi_d<PA_FP8_E4M3>(m, head_dim, stream_v, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
                          bool stream_v, int num_seqs, hipStream_t stream) {

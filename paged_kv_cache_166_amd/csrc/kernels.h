@@ -31,6 +31,31 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
                          bool stream_v, int num_seqs, hipStream_t stream);
 
+// One pool of a batch over several pools (pa_decode_multi).
+struct DecodeGroup {
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;  // this group's rows only
+  int32_t max_blocks_per_seq;
+  int32_t block_size;
+  int32_t seq_begin;            // first batch row of the group
+  int32_t pad;
+};
+
+constexpr int kMaxDecodeGroups = 8;
+
+struct DecodeMultiArgs {
+  DecodeArgs base;  // q, out, context_lens, workspace, heads, max_parts, scale, dtypes
+  int32_t num_groups;
+  int32_t part_tokens;
+  DecodeGroup g[kMaxDecodeGroups];
+};
+
+hipError_t launch_decode_multi(const DecodeMultiArgs& m, int kv_dtype, int head_dim,
+                               bool stream_v, int num_seqs, hipStream_t stream);
+
 struct CacheWriteArgs {
   void* k_cache;
   void* v_cache;

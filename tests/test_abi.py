@@ -108,3 +108,32 @@ def test_reshape_and_prefill_checks():
     assert r == pa.PA_ERR_UNSUPPORTED
     r = pa.lib.pa_copy_blocks(ctypes.byref(p), None, 3, None)
     assert r == pa.PA_ERR_INVALID
+
+
+def test_decode_multi_rejects_bad_arguments_before_launch():
+    pools = (pa._Pool * 2)(_fake_pool(block_size=16), _fake_pool(block_size=64))
+    mb = (ctypes.c_int32 * 2)(4, 2)
+    tabs = (ctypes.c_void_p * 2)(0x50000, 0x58000)
+
+    def call(pools=pools, G=2, seq_begin=(0, 1, 2), pt=0, q_dtype=pa.PA_F16):
+        sb = (ctypes.c_int32 * len(seq_begin))(*seq_begin)
+        return pa.lib.pa_decode_multi(ctypes.c_void_p(0x30000), pa.PA_F32, ctypes.c_void_p(0x40000),
+                                      q_dtype, ctypes.cast(pools, ctypes.POINTER(pa._Pool)), G,
+                                      ctypes.cast(tabs, ctypes.c_void_p), mb, sb,
+                                      ctypes.c_void_p(0x60000), 0.1, pt, None, 0, None)
+
+    assert call(pt=96) == pa.PA_ERR_UNSUPPORTED               # not a multiple of 64
+    assert call(pt=64 * 300) == pa.PA_ERR_UNSUPPORTED         # 1200 blocks of 16
+    assert call(seq_begin=(0, 2, 1)) == pa.PA_ERR_INVALID     # decreasing
+    assert call(seq_begin=(1, 1, 2)) == pa.PA_ERR_INVALID
+    assert call(G=0) == pa.PA_ERR_INVALID
+    assert call(G=9) == pa.PA_ERR_INVALID
+    assert call(q_dtype=pa.PA_BF16) == pa.PA_ERR_UNSUPPORTED  # q must match f16 KV
+    mixed = (pa._Pool * 2)(_fake_pool(block_size=16), _fake_pool(block_size=64, num_heads=3))
+    assert call(pools=mixed) == pa.PA_ERR_INVALID             # heads differ
+    # a workspace is needed: 4 blocks of 16 = 64 tokens in partitions of 32
+    assert call(pt=32) == pa.PA_ERR_UNSUPPORTED               # 32 is not a multiple of 64
+    n = pa.lib.pa_decode_multi_workspace_bytes(ctypes.cast(pools, ctypes.POINTER(pa._Pool)), mb, 2,
+                                               2, 64)
+    assert n > 0
+    assert call(pt=64) == pa.PA_ERR_INVALID                   # workspace missing

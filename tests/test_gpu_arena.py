@@ -128,6 +128,46 @@ def _decode_group(ar, b, seqs, scale):
     assert_close(out.cpu().numpy().astype(np.float64), ref, TOL[ar.kv], f"decode {ar.kv} bs={b}")
 
 
+def _decode_multi(ar, seqs, scale, pt=0):
+    """The mixed batch in one pa_decode_multi (rows grouped by size), against
+    the oracle per size, and bit for bit against pa_decode per size where
+    both use the same sub-tiles and partitions (every size but 32)."""
+    groups = sorted(ar.groups(seqs).items())
+    order = [s for _, grp in groups for s in grp]
+    qdt = "bf16" if ar.kv == "fp8" else ar.kv
+    qb = to_bits(ar.rng.standard_normal((len(order), ar.H, ar.D), dtype=np.float32), qdt)
+    q64 = C.to_float64(qb, qdt)
+    q_dev = bits_to_device(qb, qdt, "cuda")
+    pools, tables, seq_begin, lens = [], [], [0], []
+    for b, grp in groups:
+        maxb = max(len(ar.ora.block_table(s)) for s in grp)
+        t, ln = ar.lib.pack(grp, maxb)
+        pools.append(ar.pool.view(b))
+        tables.append(torch.from_numpy(t).cuda())
+        seq_begin.append(seq_begin[-1] + len(grp))
+        lens += ln.tolist()
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.full((len(order), ar.H, ar.D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = pa.decode_multi_workspace(pools, [t.shape[1] for t in tables], len(order), pt)
+    pa.pa_decode_multi(out, q_dev, pools, tables, lens_dev, seq_begin, scale, pt, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for (b, grp), pool, t, lo in zip(groups, pools, tables, seq_begin):
+        ok, ov, ks, vs = ar.oracle_kv(b)
+        rows = slice(lo, lo + len(grp))
+        ref = A.decode(q64[rows], ok, ov, ar.kv, [ar.ora.block_table(s) for s in grp],
+                       [ar.ora.seq_len(s) for s in grp], b, scale, k_scale=ks, v_scale=vs)
+        assert_close(got[rows].astype(np.float64), ref, TOL[ar.kv], f"multi {ar.kv} bs={b} pt={pt}")
+        if b != 32 and pt in (0, 512):
+            single = torch.empty((len(grp), ar.H, ar.D), dtype=torch.float32, device="cuda")
+            ws1 = pa.decode_workspace(pool, len(grp), t.shape[1], 0)
+            pa.pa_decode(single, q_dev[rows].contiguous(), pool, t, lens_dev[rows].contiguous(),
+                         scale, 0, ws1)
+            torch.cuda.synchronize()
+            assert np.array_equal(single.cpu().numpy().view(np.uint32),
+                                  got[rows].view(np.uint32)), f"bs={b}"
+
+
 @pytest.mark.parametrize("kv", ["bf16", "f16", "fp8"])
 def test_mixed_block_sizes_share_one_arena(kv):
     H, D = 4, 128
@@ -151,6 +191,7 @@ def test_mixed_block_sizes_share_one_arena(kv):
             ar.write(b, [want[ids.index(s)][0][0] for s in grp])
         for b, grp in ar.groups(ids).items():
             _decode_group(ar, b, grp, scale)
+        _decode_multi(ar, ids, scale, (0, 64, 128)[step])
     ar.check_bits()
     # free some, fork one, allocate others: memory changes size (splits and merges)
     for s in (1, 3, 5):
@@ -168,6 +209,7 @@ def test_mixed_block_sizes_share_one_arena(kv):
     ar.check_bits()
     for b, grp in ar.groups(ar.live).items():
         _decode_group(ar, b, grp, scale)
+    _decode_multi(ar, ar.live, scale)
     # prefill of new prompts, one call per size
     if kv != "fp8":
         new = {}
@@ -195,3 +237,44 @@ def test_mixed_block_sizes_share_one_arena(kv):
     for s in list(ar.live):
         ar.free(s)
     assert ar.lib.free_tokens() == ar.T == ar.ora.free_tokens()
+
+
+def test_decode_multi_over_separate_pools():
+    """Two pools that are not views of one arena (blocks of 16 and 32, f16),
+    an empty group between them, partitions of 32 to 2048 tokens, and an f16
+    output."""
+    from tests.gpu_util import Scenario, half_ulp
+    D, H = 128, 3
+    s16 = Scenario(300, H, 16, D, "f16", seed=61)
+    s32 = Scenario(200, H, 32, D, "f16", seed=62)
+    lens16, lens32 = [1, 16, 17, 700, 2000], [0, 31, 33, 1500]
+    for i, n in enumerate(lens16):
+        s16.prompt(i, n)
+    for i, n in enumerate(lens32):
+        s32.prompt(i, n)
+    t16, l16, _, _ = s16.device_tables(list(range(len(lens16))))
+    t32, l32, _, _ = s32.device_tables(list(range(len(lens32))))
+    empty = Scenario(4, H, 8, D, "f16", seed=63)
+    q_dev, q64 = s16.random_q(len(lens16) + len(lens32), "f16")
+    lens = torch.cat([l16, l32])
+    seq_begin = [0, len(lens16), len(lens16), len(lens16) + len(lens32)]
+    pools = [s16.pool, empty.pool, s32.pool]
+    tables = [t16, None, t32]
+    scale = 1 / math.sqrt(D)
+    ref = np.concatenate([
+        A.decode(q64[:5], s16.ok, s16.ov, "f16", *s16.oracle_tables(list(range(5))), 16, scale),
+        A.decode(q64[5:], s32.ok, s32.ov, "f16", *s32.oracle_tables(list(range(4))), 32, scale)])
+    for pt in (32, 64, 512, 2048, 0):
+        out = torch.full(q_dev.shape, float("nan"), dtype=torch.float32, device="cuda")
+        ws = pa.decode_multi_workspace(pools, [t16.shape[1], 1, t32.shape[1]], 9, pt)
+        pa.pa_decode_multi(out, q_dev, pools, tables, lens, seq_begin, scale, pt, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert_close(got, ref, TOL["f16"], f"pt={pt}")
+        assert np.all(got[5] == 0.0)                          # empty sequence
+    out = torch.empty(q_dev.shape, dtype=torch.float16, device="cuda")
+    pa.pa_decode_multi(out, q_dev, pools, tables, lens, seq_begin, scale, 64,
+                       pa.decode_multi_workspace(pools, [t16.shape[1], 1, t32.shape[1]], 9, 64))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= TOL["f16"] + half_ulp("f16", ref))
