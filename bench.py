@@ -307,7 +307,10 @@ class DecodeBench:
         rule gives their length (one pa_decode per size, back to back on the
         stream, timed as one).  Event-timed medians, warm caches; bytes =
         this launch's algorithmic bytes (K/V rows, q, out; tables at each
-        size).  Memory: tokens reserved (whole blocks) against tokens held."""
+        size).  Memory: tokens reserved (whole blocks) against tokens held.
+        The pools here do not set the stream flag (ordinary loads for K and
+        V), so these launches are kernels of their own in a profile, apart
+        from the steps' pa_decode."""
         lens = self.lens_now()
         H, D, B = self.H, self.D, self.B
         row = H * D * ELEM[self.kv]
@@ -347,7 +350,7 @@ class DecodeBench:
             alloc = pa.Allocator(N, bs, W.free_order(self.cfg["seed"] + bs, N))
             for i in range(B):
                 alloc.alloc_prompt(i, int(lens[i]))
-            pool = pa.PagedPool.empty(N, H, bs, D, self.kv, self.device, stream_kv=self.stream_kv)
+            pool = pa.PagedPool.empty(N, H, bs, D, self.kv, self.device)
             fill(pool.k_cache, pool.v_cache)
             maxb = int(np.max(-(-lens // bs)))
             t, ln = alloc.pack(self.ids, maxb)
@@ -362,7 +365,7 @@ class DecodeBench:
         arena_tokens = -(-int(np.sum(-(-lens // 64) * 64)) // 64) * 64 + 64 * 64
         ba = pa.BuddyAllocator(arena_tokens, W.free_order(self.cfg["seed"], arena_tokens // 64))
         sizes = np.array([ba.alloc_prompt(i, int(lens[i]))[0] for i in range(B)])
-        arena = pa.ArenaPool(arena_tokens, H, D, self.kv, self.device, stream_kv=self.stream_kv)
+        arena = pa.ArenaPool(arena_tokens, H, D, self.kv, self.device)
         fill(arena.k, arena.v)
         calls, groups, keep = [], [], []
         mpools, mtabs, mbegin, mrows = [], [], [0], []
@@ -783,6 +786,9 @@ def main():
     ap.add_argument("--workload", default="llama13b_decode",
                     choices=["llama13b_decode", "prefix_cow", "chunked_prefill", "long_fp8_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed steps: no cold-cache series, block-size, fp8-write, "
+                         "prefix-reuse or eviction measurements (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the reference "
                          "for scaling HBM byte counters) and exit")
@@ -858,6 +864,7 @@ def main():
         res["hbm_frac_step"] = kv_bytes * b.layers / step_s / 1e9 / HBM_PEAK_GBS
         res["decode_tokens_per_s"] = b.B / step_s
         res["pa_decode_us_per_layer"] = kt * 1e6
+    if args.workload != "chunked_prefill" and not args.no_extras:
         log("bench: cold-cache series")
         res["cold"] = b.cold_series()
         if args.workload == "llama13b_decode":
