@@ -278,3 +278,22 @@ def test_decode_multi_over_separate_pools():
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ref) <= TOL["f16"] + half_ulp("f16", ref))
+
+
+def test_llama13b_batch_by_the_size_rule():
+    """The LLaMA-13B decode batch (32 sequences of 128..2048 tokens, seeded;
+    40 heads x 128, fp16) in one arena by the size rule, decoded in one
+    pa_decode_multi launch as the bench times it: all 1280 (sequence, head)
+    outputs against the oracle, and bit for bit against pa_decode per size
+    (every size but 32)."""
+    import workloads as W
+    cfg = W.CONFIGS["llama13b_decode"]
+    lens = [int(x) for x in W.uniform_ints(cfg["seed"], cfg["batch"], cfg["len_lo"], cfg["len_hi"])]
+    tokens = sum(-(-n // 64) * 64 for n in lens) + 64 * 64
+    ar = Arena(tokens, cfg["num_heads"], cfg["head_dim"], "f16", seed=cfg["seed"])
+    for i, n in enumerate(lens):
+        ar.prompt(i, n)
+    sizes = {ar.ora.block_size(i) for i in range(len(lens))}
+    assert sizes == {8, 16, 32, 64}
+    ar.check_bits()
+    _decode_multi(ar, list(range(len(lens))), 1 / math.sqrt(cfg["head_dim"]))
