@@ -172,6 +172,9 @@ class DecodeBench:
         self.stream_kv = (workload != "prefix_cow") if stream_kv is None else stream_kv
         # fp8: the step's appended tokens keep each block's scale at its amax / 448
         self.auto_scale = self.kv == "fp8"
+        # 16-bit pools: the step's new rows are stored by the decode launch
+        # itself (pa_decode_append); fp8 pools write them first (scale upkeep)
+        self.fused = self.kv != "fp8"
         self.lens0 = lens0
         self.alloc = pa.Allocator(self.N, self.bs, W.free_order(cfg["seed"], self.N))
         g = torch.Generator(device=device)
@@ -240,8 +243,9 @@ class DecodeBench:
         for li, pool in enumerate(self.pools):
             if pairs is not None:
                 pa.pa_copy_blocks(pool, pairs)
-            pa.pa_reshape_and_cache(pool, self.knew[(k + li) % 4], self.vnew[(k + li) % 4],
-                                    d["slots"].view(-1))
+            if not self.fused:
+                pa.pa_reshape_and_cache(pool, self.knew[(k + li) % 4], self.vnew[(k + li) % 4],
+                                        d["slots"].view(-1))
             # one launch per step carries the event pair (an event record
             # waits for the caches to be written back, which would otherwise
             # stall every layer): a middle layer, in the steady state -- the
@@ -250,8 +254,13 @@ class DecodeBench:
             if timing:
                 tm = Timer()
                 tm.start()
-            pa.pa_decode(self.out, self.q[(k + li) % 4], pool, d["tables"], d["lens"], self.scale,
-                         self.pb, self.ws)
+            if self.fused:
+                pa.pa_decode_append(self.out, self.q[(k + li) % 4], pool, self.knew[(k + li) % 4],
+                                    self.vnew[(k + li) % 4], d["slots"].view(-1), d["tables"],
+                                    d["lens"], self.scale, self.pb, self.ws)
+            else:
+                pa.pa_decode(self.out, self.q[(k + li) % 4], pool, d["tables"], d["lens"],
+                             self.scale, self.pb, self.ws)
             if timing:
                 tm.stop()
                 self.ev.append(tm)
@@ -594,7 +603,8 @@ class DecodeBench:
 
     def decode_bytes(self, lens):
         """Algorithmic bytes of one pa_decode launch: every cached K and V row
-        once, q, out, the table entries read and the lengths."""
+        once, q, out, the table entries read and the lengths (and, for
+        pa_decode_append, the new rows stored)."""
         row = self.H * self.D * ELEM[self.kv]
         kv = 2 * int(np.sum(lens)) * row
         qo = self.B * self.H * self.D * (ELEM[self.qdt] * 2)
@@ -602,7 +612,8 @@ class DecodeBench:
         scales = 0
         if self.kv == "fp8":
             scales = 2 * int(np.sum(-(-lens // self.bs))) * self.H * 4
-        return kv + qo + tables + scales
+        new_rows = 2 * self.B * self.H * self.D * ELEM[self.kv] if self.fused else 0
+        return kv + qo + tables + scales + new_rows
 
     def kernel_stats(self):
         """Mean pa_decode launch time (s) and mean algorithmic bytes per launch."""
@@ -859,7 +870,8 @@ def main():
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS,
                            "traffic": measured_traffic(args.workload, "decode_kernel"),
-                           "kernel": "pa_decode (decode_kernel + decode_merge_kernel)",
+                           "kernel": ("pa_decode_append" if b.fused else "pa_decode")
+                           + " (decode_kernel + decode_merge_kernel)",
                            "kernel_us": kt * 1e6, "bytes_per_launch": kv_bytes}
         res["hbm_frac_step"] = kv_bytes * b.layers / step_s / 1e9 / HBM_PEAK_GBS
         res["decode_tokens_per_s"] = b.B / step_s

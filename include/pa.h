@@ -180,6 +180,29 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_append -- pa_reshape_and_cache of each sequence's new token,
+ * then pa_decode, in one launch (same results, same cache contents).  The
+ * new row belongs to position context_lens[i] - 1 of sequence i: the
+ * workgroup that covers that position stores the row at new_slots[i] and
+ * uses it from registers, so the row is never read back in this call.
+ *   key_new, value_new  device, [num_seqs][num_heads][head_dim] of the pool's
+ *                 KV type (f32, f16 or bf16 pools; fp8 pools: PA_ERR_UNSUPPORTED,
+ *                 their rows go through pa_reshape_and_cache), 16-byte aligned.
+ *   new_slots     device, [num_seqs] int64: the slot of position
+ *                 context_lens[i] - 1 (what pa_append_tokens returned);
+ *                 < 0: no row for that sequence (nothing stored, the cache is
+ *                 read as it is).  The slot's block must not be shared (copy it
+ *                 first, as for any write).
+ * Other arguments, layout and errors as pa_decode.
+ */
+pa_status pa_decode_append(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                           const pa_pool* pool, const void* key_new, const void* value_new,
+                           const int64_t* new_slots, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, float scale, int32_t partition_blocks,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pa_decode_multi -- pa_decode of one batch whose sequences live in several
  * pools with the same num_heads, head_dim and kv_dtype (typically the
  * block-size views of one arena, pa_buddy_*), in one launch (plus the merge

@@ -38,7 +38,7 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
 EXPORTS = [
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_auto_partition_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_chunk",
-    "pa_decode_multi_workspace_bytes", "pa_decode_multi",
+    "pa_decode_multi_workspace_bytes", "pa_decode_multi", "pa_decode_append",
     "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_prompt", "pa_append_tokens",
     "pa_append_tokens_batch", "pa_fork", "pa_free_seq", "pa_get_block_table",
     "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
@@ -78,6 +78,8 @@ def _load():
         "pa_decode_auto_partition_blocks": (I32, [P, I32, I32]),
         "pa_decode_workspace_bytes": (SZ, [P, I32, I32, I32]),
         "pa_decode": (I32, [VP, I32, VP, I32, P, VP, I32, VP, I32, ctypes.c_float, I32, VP, SZ, VP]),
+        "pa_decode_append": (I32, [VP, I32, VP, I32, P, VP, VP, VP, VP, I32, VP, I32,
+                                   ctypes.c_float, I32, VP, SZ, VP]),
         "pa_decode_multi_workspace_bytes": (SZ, [P, pi32, I32, I32, I32]),
         "pa_decode_multi": (I32, [VP, I32, VP, I32, P, I32, VP, pi32, pi32, VP, ctypes.c_float, I32,
                                   VP, SZ, VP]),
@@ -294,6 +296,24 @@ def pa_prefill_chunk(out, q, pool, block_tables, context_lens, query_start_loc, 
                                 _ptr(block_tables), maxb, _ptr(context_lens),
                                 _ptr(query_start_loc), B, int(max_query_len), float(scale),
                                 _stream(stream, pool.device)), "pa_prefill_chunk")
+
+
+def pa_decode_append(out, q, pool, key_new, value_new, new_slots, block_tables, context_lens,
+                     scale, partition_blocks=0, workspace=None, stream=None):
+    """pa_reshape_and_cache of each sequence's new row (position L - 1, at
+    new_slots [B] int64) and pa_decode, in one launch; key_new/value_new
+    [B, H, D] of the pool's type."""
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert new_slots.dtype == torch.int64 and key_new.dtype == value_new.dtype
+    for t in (block_tables, q, out, key_new, value_new, new_slots):
+        assert t.is_contiguous()
+    B, maxb = block_tables.shape
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib.pa_decode_append(_ptr(out), dtype_code(out), _ptr(q), dtype_code(q), pool.ref(),
+                                _ptr(key_new), _ptr(value_new), _ptr(new_slots), _ptr(block_tables),
+                                maxb, _ptr(context_lens), B, float(scale), int(partition_blocks),
+                                _ptr(workspace), ws_bytes, _stream(stream, pool.device)),
+           "pa_decode_append")
 
 
 def _pool_array(pools):

@@ -164,12 +164,18 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
   return size_t(ws_layout(pool, num_seqs, max_blocks_per_seq, pb).bytes);
 }
 
-pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
-                    const pa_pool* pool, const int32_t* block_tables,
-                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                    float scale, int32_t partition_blocks, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "pa_decode";
+}  // extern "C"
+
+namespace {
+
+// pa_decode, and pa_decode_append when key_new is not NULL.
+pa_status decode_impl(const char* fn, void* out, int32_t out_dtype, const void* q,
+                      int32_t q_dtype, const pa_pool* pool, const void* key_new,
+                      const void* value_new, const int64_t* new_slots,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, float scale,
+                      int32_t partition_blocks, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
   if (pa_status s = check_pool(fn, pool)) return s;
   if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "%s: num_seqs %d", fn, num_seqs);
   if (num_seqs == 0) return PA_OK;
@@ -216,9 +222,46 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
   a.scale_log2 = scale * 1.4426950408889634f;
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
+  if (key_new) {
+    if (pool->kv_dtype == PA_FP8_E4M3)
+      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 pools write new rows with pa_reshape_and_cache",
+                  fn);
+    if (!value_new || !new_slots) return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+    if (!aligned(key_new, 16) || !aligned(value_new, 16) || !aligned(new_slots, 8))
+      return fail(PA_ERR_INVALID, "%s: key_new/value_new must be 16-byte aligned", fn);
+    a.k_new = key_new;
+    a.v_new = value_new;
+    a.new_slots = new_slots;
+  }
   return hip_status(fn, pa::launch_decode(a, pool->kv_dtype, pool->head_dim, pool->block_size,
                                           (pool->flags & PA_POOL_STREAM_KV) != 0, num_seqs,
                                           stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                    const pa_pool* pool, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    float scale, int32_t partition_blocks, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl("pa_decode", out, out_dtype, q, q_dtype, pool, nullptr, nullptr, nullptr,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, scale,
+                     partition_blocks, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                           const pa_pool* pool, const void* key_new, const void* value_new,
+                           const int64_t* new_slots, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, float scale, int32_t partition_blocks,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!key_new) return fail(PA_ERR_INVALID, "pa_decode_append: key_new is NULL");
+  return decode_impl("pa_decode_append", out, out_dtype, q, q_dtype, pool, key_new, value_new,
+                     new_slots, block_tables, max_blocks_per_seq, context_lens, num_seqs, scale,
+                     partition_blocks, workspace, workspace_bytes, stream);
 }
 
 size_t pa_decode_multi_workspace_bytes(const pa_pool* pools, const int32_t* max_blocks_per_seq,

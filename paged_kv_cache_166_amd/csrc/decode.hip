@@ -193,7 +193,11 @@ constexpr int kMaxPartBlocks = 256;
 constexpr int default_max_loads(int bs) { return bs >= 64 ? 4 : 8; }
 
 // One workgroup's work: (head, sequence, partition) = blockIdx (x, y, z).
-template <int KV, int D, int BS, int NW, bool kStreamV, int MaxL>
+// kAppend (16-bit and fp32 pools): the step's new K/V row of each sequence
+// (position L - 1) comes with the call; the workgroup of the last partition
+// stores it at its slot and uses it from registers for that position, so no
+// wave reads the row while it is being written.
+template <int KV, int D, int BS, int NW, bool kStreamV, int MaxL, bool kAppend = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G = Geo<KV, D, BS, MaxL>;
   using Ops = KvOps<KV>;
@@ -237,6 +241,22 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   if (part >= nparts) return;
   const int nb = min(a.part_blocks, nblocks - blk0);
   const bool row_ok = !G::kIdleGroups || grp < BS;
+
+  // The new row (kAppend): the wave that owns the partition's last block
+  // (the one holding position L - 1) loads it, 16 bytes per lane (this
+  // lane's column), and stores it after the loop (a store here would wait
+  // for these loads before any tile load could go out).
+  uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+  int64_t new_slot = -1;
+  if constexpr (kAppend) {
+    if (part == nparts - 1 && wave == (nb - 1) % NW) new_slot = a.new_slots[seq];
+    if (new_slot >= 0) {
+      const int64_t off = (out_off + col * E) * G::kElem;
+      knew = *(const uint4*)((const char*)a.k_new + off);
+      vnew = *(const uint4*)((const char*)a.v_new + off);
+    }
+  }
+  const bool has_new = new_slot >= 0;
 
   // This wave's blocks are wave, wave + NW, ... of the partition (n_w <= 64
   // of them); lane t of `tab` holds the block id of the wave's t-th block.
@@ -295,6 +315,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int r0 = (blk0 + jl) * BS + (u % G::kSubs) * G::kSubRows;  // first token of the unit
     const int tok0 = r0 + grp;                    // token of load 0 in this lane's group
     const bool full = r0 + G::kSubRows <= L;
+    if constexpr (kAppend) {
+      if (has_new && r0 + G::kSubRows >= L) {   // the unit holding position L - 1
+#pragma unroll
+        for (int i = 0; i < G::kLoads; ++i) {
+          if (tok0 + i * G::kRows == L - 1) {
+            kr[i] = knew;
+            vr[i] = vnew;
+          }
+        }
+      }
+    }
     float s[G::kLoads];
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
@@ -340,6 +371,15 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       issue(k0, v0, p0, i + 1);
       consume(k1, v1, p1, i);
       if (++i >= n_u) break;
+    }
+  }
+
+  if constexpr (kAppend) {
+    if (has_new && lane < G::kLpr) {   // one lane group stores the row
+      const int64_t dst =
+          ((new_slot / BS * H + head) * BS + new_slot % BS) * G::kRowBytes + lane * 16;
+      *(uint4*)((char*)a.k_cache + dst) = knew;
+      *(uint4*)((char*)a.v_cache + dst) = vnew;
     }
   }
 
@@ -396,9 +436,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   }
 }
 
-template <int KV, int D, int BS, int NW, bool kStreamV>
+template <int KV, int D, int BS, int NW, bool kStreamV, bool kAppend>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  decode_body<KV, D, BS, NW, kStreamV, default_max_loads(BS)>(a);
+  decode_body<KV, D, BS, NW, kStreamV, default_max_loads(BS), kAppend>(a);
 }
 
 // A batch over several pools (same heads, head_dim and KV type; e.g. the
@@ -501,12 +541,24 @@ constexpr int kWaves = 4;
 template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_t stream) {
   dim3 grid(a.num_heads, num_seqs, a.max_parts);
-  if (stream_v)
-    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true>), grid, dim3(kWaves * 64), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false>), grid, dim3(kWaves * 64), 0,
-                       stream, a);
+  constexpr bool kCanAppend = KV != PA_FP8_E4M3;
+  if (a.k_new && !kCanAppend) return hipErrorInvalidValue;
+  if (a.k_new) {
+    if constexpr (kCanAppend) {
+      if (stream_v)
+        hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, true>), grid,
+                           dim3(kWaves * 64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, true>), grid,
+                           dim3(kWaves * 64), 0, stream, a);
+    }
+  } else if (stream_v) {
+    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, false>), grid, dim3(kWaves * 64),
+                       0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, false>), grid, dim3(kWaves * 64),
+                       0, stream, a);
+  }
   constexpr int R = 512 / D;
   if (a.max_parts > 1)
     hipLaunchKernelGGL((decode_merge_kernel<D, R>), dim3(a.num_heads, num_seqs), dim3(D * R), 0,

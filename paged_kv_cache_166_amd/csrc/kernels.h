@@ -26,6 +26,11 @@ struct DecodeArgs {
   float scale_log2;  // scale * log2(e)
   int32_t q_dtype;
   int32_t out_dtype;
+  // pa_decode_append only (else NULL): the new row of each sequence,
+  // [num_seqs][num_heads][head_dim] of the KV type, and its slot (< 0: none)
+  const void* k_new;
+  const void* v_new;
+  const int64_t* new_slots;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
