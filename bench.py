@@ -65,6 +65,13 @@ def measured_traffic(workload, kernel):
     return None
 
 
+def spread(seconds):
+    """Median, 10th and 90th percentile of event-timed launches, in us."""
+    us = np.asarray(seconds) * 1e6
+    return {"launches": int(us.size), "p10": float(np.percentile(us, 10)),
+            "median": float(np.median(us)), "p90": float(np.percentile(us, 90))}
+
+
 class Timer:
     """HIP events (torch.cuda.Event, timing enabled) recorded on the launch
     stream immediately before and after one call."""
@@ -620,6 +627,9 @@ class DecodeBench:
         times = [t.seconds() for t in self.ev]
         return float(np.mean(times)), float(np.mean(self.step_bytes))
 
+    def kernel_spread(self):
+        return spread([t.seconds() for t in self.ev])
+
     def workload_config(self):
         c = self.cfg
         d = {"workload": self.name, "layers_per_step": self.layers, "batch": self.B,
@@ -736,6 +746,9 @@ class PrefillBench:
     def kernel_stats(self):
         t = float(np.mean([tm.seconds() for tm in self.ev]))
         return t, self.flops()
+
+    def kernel_spread(self):
+        return spread([tm.seconds() for tm in self.ev])
 
     def hbm_bytes(self):
         """Algorithmic bytes of one launch: every context and chunk K/V row
@@ -856,7 +869,8 @@ def main():
         res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
                            "traffic": measured_traffic(args.workload, "prefill_kernel"),
-                           "kernel": "prefill_kernel", "kernel_us": kt * 1e6}
+                           "kernel": "prefill_kernel", "kernel_us": kt * 1e6,
+                           "kernel_us_spread": b.kernel_spread()}
         hb = b.hbm_bytes()
         res["hbm"] = {"bytes_per_launch": hb, "GBps": hb / kt / 1e9,
                       "frac": hb / kt / 1e9 / HBM_PEAK_GBS}
@@ -872,7 +886,8 @@ def main():
                            "traffic": measured_traffic(args.workload, "decode_kernel"),
                            "kernel": ("pa_decode_append" if b.fused else "pa_decode")
                            + " (decode_kernel + decode_merge_kernel)",
-                           "kernel_us": kt * 1e6, "bytes_per_launch": kv_bytes}
+                           "kernel_us": kt * 1e6, "kernel_us_spread": b.kernel_spread(),
+                           "bytes_per_launch": kv_bytes}
         res["hbm_frac_step"] = kv_bytes * b.layers / step_s / 1e9 / HBM_PEAK_GBS
         res["decode_tokens_per_s"] = b.B / step_s
         res["pa_decode_us_per_layer"] = kt * 1e6
