@@ -89,3 +89,82 @@ def test_fp8_pools_are_refused():
     with pytest.raises(NotImplementedError):
         pa.pa_decode_append(out, q, sc.pool, kn, kn, torch.zeros(1, dtype=torch.int64, device="cuda"),
                             t_dev, ln_dev, 0.1)
+
+
+def _append_step(sc, seqs, stream):
+    """One decode step as the bench runs it: batch append in the allocators,
+    copies for shared last blocks, then pa_decode_append with the new rows."""
+    import workloads as W  # noqa: F401
+    slots_lib, cow_lib, _ = sc.alloc.append_tokens_batch(seqs, 1)
+    want = sc.ora.append_tokens_batch(seqs, 1)
+    assert [list(r) for r in slots_lib] == [w[0] for w in want]
+    pairs = [w[1] for w in want if w[1] is not None]
+    if pairs:
+        pa.pa_copy_blocks(sc.pool, torch.tensor(pairs, dtype=torch.int32, device="cuda"))
+        C.copy_blocks(sc.ok, pairs)
+        C.copy_blocks(sc.ov, pairs)
+    slots = [w[0][0] for w in want]
+    H, D, kv = sc.H, sc.D, sc.kv
+    kb = to_bits(sc.rng.standard_normal((len(seqs), H, D), dtype=np.float32), kv)
+    vb = to_bits(sc.rng.standard_normal((len(seqs), H, D), dtype=np.float32), kv)
+    C.write_rows(sc.ok, kb, slots, sc.bs)
+    C.write_rows(sc.ov, vb, slots, sc.bs)
+    q_dev, q64 = sc.random_q(len(seqs), kv)
+    t_dev, ln_dev, _, _ = sc.device_tables(seqs)
+    sc.pool.stream_kv = stream
+    out = torch.full((len(seqs), H, D), float("nan"), dtype=torch.float32, device="cuda")
+    pa.pa_decode_append(out, q_dev, sc.pool, bits_to_device(kb, kv, "cuda"),
+                        bits_to_device(vb, kv, "cuda"),
+                        torch.tensor(slots, dtype=torch.int64, device="cuda"), t_dev, ln_dev,
+                        1 / math.sqrt(D), 0, pa.decode_workspace(sc.pool, len(seqs), t_dev.shape[1]))
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), q64, len(pairs)
+
+
+def test_llama13b_step_as_benchmarked():
+    """The LLaMA-13B decode batch (32 sequences of 128..2048 tokens after the
+    step, 40 heads x 128, fp16, block 16, shuffled 4096-block pool), one step
+    through pa_decode_append with the stream flag: the whole pool bit for bit
+    and all 1280 outputs against the oracle."""
+    import workloads as W
+    cfg = W.CONFIGS["llama13b_decode"]
+    lens = W.uniform_ints(cfg["seed"], cfg["batch"], cfg["len_lo"], cfg["len_hi"])
+    sc = Scenario(cfg["num_blocks"], cfg["num_heads"], cfg["block_size"], cfg["head_dim"], "f16",
+                  seed=cfg["seed"])
+    for i, L in enumerate(lens):
+        sc.prompt(i, int(L) - 1)
+    seqs = list(range(cfg["batch"]))
+    got, q64, ncow = _append_step(sc, seqs, stream=True)
+    assert ncow == 0
+    sc.check_pool_bits()
+    ref = _oracle(sc, seqs, q64, 1 / math.sqrt(cfg["head_dim"]))
+    assert_close(got, ref, TOL["f16"], "llama13b append step")
+
+
+def test_prefix_cow_step_as_benchmarked():
+    """64 sequences sharing a 1024-token prefix plus 1..256 own tokens (bf16,
+    block 16), one step through pa_decode_append; then a fork in the middle of
+    a block whose next step copies the shared block before the new row is
+    stored by the decode launch."""
+    import workloads as W
+    cfg = W.CONFIGS["prefix_cow"]
+    B = cfg["batch"]
+    sc = Scenario(cfg["num_blocks"], cfg["num_heads"], cfg["block_size"], cfg["head_dim"], "bf16",
+                  seed=cfg["seed"])
+    sc.prompt(0, cfg["prefix"])
+    for i in range(1, B):
+        sc.fork(0, i)
+    suffix = W.uniform_ints(cfg["seed"], B, cfg["suffix_lo"], cfg["suffix_hi"])
+    for i in range(B):
+        sc.append(i, int(suffix[i]))
+    seqs = list(range(B))
+    scale = 1 / math.sqrt(cfg["head_dim"])
+    got, q64, _ = _append_step(sc, seqs, stream=False)
+    sc.check_pool_bits()
+    assert_close(got, _oracle(sc, seqs, q64, scale), TOL["bf16"], "prefix append step")
+    p = next(i for i in range(B) if sc.ora.seq_len(i) % cfg["block_size"] != 0)
+    sc.fork(p, B)
+    got2, q2, ncow = _append_step(sc, [p, B], stream=False)
+    assert ncow == 1                         # the child's write copies the shared block first
+    sc.check_pool_bits()
+    assert_close(got2, _oracle(sc, [p, B], q2, scale), TOL["bf16"], "after CoW")
