@@ -825,8 +825,8 @@ def main():
                     help="decode pools' PA_POOL_STREAM_KV flag (auto: on unless blocks are shared)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(each GPU would hold its own pool and batch; see the sharding notes).",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(each GPU would hold its own pools and sub-batch).",
               file=sys.stderr)
         sys.exit(2)
     device = "cuda:0"

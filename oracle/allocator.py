@@ -15,7 +15,7 @@ Follows the block manager the pages describe:
   a per-request block table, a free list that freed blocks return to, and
   blocks returned when the request ends.
 
-Readings where the pages are silent (each one listed in the design doc):
+Readings where the pages are silent:
 
 * The free list is FIFO: initial order is the caller's (default 0..N-1),
   allocation pops the front, freed blocks go to the back in table order.

@@ -12,7 +12,7 @@ pseudocode).  So the oracle is the plain definition, written out:
 
 (PagedAttention blog article, section 3.2.2 forward pass: gather, Q K^T
 divided by sqrt(head_dim), causal mask, softmax, weighted sum of V, output
-zero-initialised.)  Readings of that listing, each in the design doc:
+zero-initialised.)  Readings of that listing:
 
 * scores are per head, Q_h K_h^T (the listing's matmul shapes do not line up);
 * one softmax over all visible keys (the course pseudocode puts it inside the

@@ -2,7 +2,7 @@
 
 The first page's "3.0" feature list: the page (block) size is adjusted to the
 request's length, blocks of different sizes serve requests of different
-lengths, to use memory better.  Readings (listed in the design doc):
+lengths, to use memory better.  Readings where the page is silent:
 
 * sizes: 8, 16, 32 and 64 tokens.  Memory is one arena of 8-token units; a
   block of 8 * 2^k tokens (order k) is 2^k consecutive units starting at a

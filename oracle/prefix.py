@@ -25,7 +25,7 @@ oracle is that flat list, in insertion order, tied to the oracle allocator:
   each entry's blocks by index; a block reaching zero goes back to the free
   list.
 
-Readings (listed in the design doc): the match is at token granularity (a partly
+Readings where the notes are silent: the match is at token granularity (a partly
 filled last block is shared and copied on the first write, as the allocator's
 copy-on-write does); a full hit leaves an empty suffix (a caller wanting the
 last token recomputed matches one token fewer); ties between equal LCPs take

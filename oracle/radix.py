@@ -13,7 +13,7 @@ its blocks from its divergence point on, block j of a hit comes from the
 creator of the node holding position min((j+1) bs, h) - 1.  Without eviction
 the two oracles must agree exactly (a pin of each by the other).
 
-Readings for eviction (listed in DESIGN.md):
+Readings for eviction, where the notes are silent:
 
 * use: an insertion or a cached-prompt allocation stamps every node its walk
   entered with the operation's clock value (a split gives the new upper node
