@@ -375,9 +375,13 @@ pa_status pa_alloc_prompt_cached(pa_prefix_index* x, int64_t seq_id, const int32
  * list in that order). */
 pa_status pa_prefix_clear(pa_prefix_index* x);
 
-/* [0] entries, [1] live tree nodes (root included), [2] block references
- * held, [3] leaves evicted so far. */
-pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out4);
+/* [0] entries inserted since creation or the last clear, [1] live tree nodes
+ * (root included), [2] block references held, [3] leaves evicted so far,
+ * [4] node slots in memory (live nodes plus evicted ones not yet dropped:
+ * evicted nodes and the entries nothing uses any more are dropped once they
+ * outnumber the live nodes by more than 64, so memory stays proportional to
+ * what is cached). */
+pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out5);
 
 /* Switch automatic eviction on (enable != 0) or off for x.  While on, an
  * allocating call on x's allocator (pa_alloc_prompt, pa_append_tokens,

@@ -666,8 +666,8 @@ class PrefixIndex:
         _check(lib.pa_prefix_clear(self._h), "pa_prefix_clear")
 
     def stats(self):
-        out = self._np.zeros(4, dtype=self._np.int64)
+        out = self._np.zeros(5, dtype=self._np.int64)
         _check(lib.pa_prefix_stats(self._h, _i64p(out)), "pa_prefix_stats")
         return {"entries": int(out[0]), "nodes": int(out[1]), "referenced_blocks": int(out[2]),
-                "evicted": int(out[3])}
+                "evicted": int(out[3]), "node_slots": int(out[4])}
 

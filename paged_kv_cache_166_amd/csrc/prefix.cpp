@@ -62,6 +62,7 @@ struct Entry {
   int64_t ref_base = 0;        // block index of refs[0]
   std::vector<int32_t> refs;   // block referenced at each index from ref_base, -1 once dropped
   int64_t held = 0;            // references still held
+  int32_t live_nodes = 0;      // live tree nodes this entry created (0: nothing uses it)
 };
 
 // What one eviction changed, so that a failed reclaim can put it back.
@@ -87,6 +88,8 @@ struct pa_prefix_index {
   std::set<std::pair<uint64_t, int32_t>> leaves;  // (stamp, node) of every live leaf
   uint64_t clock = 0;
   int64_t evicted = 0;
+  int64_t inserted = 0;   // entries inserted since creation or the last clear
+  int64_t live = 1;       // live nodes (the root included)
 
   bool is_leaf(int32_t id) const { return id != 0 && nodes[id].alive && nodes[id].kids.empty(); }
 
@@ -173,6 +176,8 @@ struct pa_prefix_index {
     leaves.erase({L.stamp, id});
     P.kids.erase(L.edge[0]);
     L.alive = false;
+    --e.live_nodes;
+    --live;
     r.parent_became_leaf = parent_leaf;
     return r;
   }
@@ -183,6 +188,8 @@ struct pa_prefix_index {
     Entry& e = entries[L.creator];
     if (r.parent_became_leaf) leaves.erase({P.stamp, L.parent});
     L.alive = true;
+    ++e.live_nodes;
+    ++live;
     P.kids[L.edge[0]] = r.leaf;
     leaves.insert({L.stamp, r.leaf});
     for (auto it = r.released.rbegin(); it != r.released.rend(); ++it) {
@@ -191,6 +198,47 @@ struct pa_prefix_index {
       ++alloc->refs[b];
       e.refs[it->first - e.ref_base] = b;
       ++e.held;
+    }
+  }
+
+  // Evicted nodes keep their ids (ties go to the older node) and entries
+  // their numbers; once the dead outnumber the live nodes (plus a margin),
+  // both are renumbered in order, dropping the dead nodes and the entries no
+  // live node uses (they hold no reference any more).  Order is all that the
+  // ids decide, so nothing observable changes.  Never called while node ids
+  // are held (a walk's segments, an undo log).
+  void maybe_compact() {
+    const int64_t dead = int64_t(nodes.size()) - live;
+    if (dead <= live + 64) return;
+    try {
+      std::vector<int32_t> emap(entries.size(), -1), nmap(nodes.size(), -1);
+      std::vector<Entry> ne;
+      std::vector<Node> nn;
+      int32_t k = 0;
+      for (size_t i = 0; i < entries.size(); ++i)
+        if (entries[i].live_nodes > 0) emap[i] = k++;
+      ne.reserve(size_t(k));
+      k = 0;
+      for (size_t i = 0; i < nodes.size(); ++i)
+        if (nodes[i].alive) nmap[i] = k++;
+      nn.reserve(size_t(k));
+      for (size_t i = 0; i < entries.size(); ++i)
+        if (emap[i] >= 0) ne.push_back(std::move(entries[i]));
+      for (size_t i = 0; i < nodes.size(); ++i) {
+        if (nmap[i] < 0) continue;
+        Node nd = std::move(nodes[i]);
+        nd.parent = nd.parent >= 0 ? nmap[nd.parent] : -1;
+        nd.creator = nd.creator >= 0 ? emap[nd.creator] : -1;
+        for (auto& kv : nd.kids) kv.second = nmap[kv.second];
+        nn.push_back(std::move(nd));
+      }
+      std::set<std::pair<uint64_t, int32_t>> nl;
+      for (const auto& lf : leaves) nl.insert({lf.first, nmap[lf.second]});
+      entries.swap(ne);
+      nodes.swap(nn);
+      leaves.swap(nl);
+    } catch (const std::bad_alloc&) {
+      // the index is untouched until the swaps: keep it as it is
     }
   }
 
@@ -218,7 +266,9 @@ struct pa_prefix_index {
 };
 
 bool pa_alloc::reclaim(pa_prefix_index* x, const std::function<bool()>& fits) {
-  return x->reclaim(fits, {});
+  const bool ok = x->reclaim(fits, {});
+  x->maybe_compact();
+  return ok;
 }
 
 extern "C" {
@@ -243,6 +293,8 @@ pa_status pa_prefix_clear(pa_prefix_index* x) {
   x->nodes.clear();
   x->nodes.emplace_back();
   x->leaves.clear();
+  x->inserted = 0;
+  x->live = 1;
   return PA_OK;
 }
 
@@ -295,6 +347,8 @@ pa_status pa_prefix_insert(pa_prefix_index* x, int64_t seq_id, const int32_t* to
         up.creator = low.creator;
         up.parent = low.parent;
         up.stamp = low.stamp;
+        ++x->entries[low.creator].live_nodes;
+        ++x->live;
         const int32_t up_id = int32_t(x->nodes.size());
         x->nodes[low.parent].kids[low.edge[0]] = up_id;  // the parent's link now points at up
         up.kids[low.edge[stop_off]] = stop_node;
@@ -315,9 +369,12 @@ pa_status pa_prefix_insert(pa_prefix_index* x, int64_t seq_id, const int32_t* to
       x->nodes.push_back(std::move(leaf));
       x->nodes[parent].kids[tokens[d]] = leaf_id;
       x->leaves.insert({x->clock, leaf_id});
+      e.live_nodes = 1;
+      ++x->live;
     }
     for (int32_t b : e.refs) ++a->refs[b];
     x->entries.push_back(std::move(e));
+    ++x->inserted;
     if (divergence) *divergence = int32_t(d);
   } catch (const std::bad_alloc&) {
     return pa::fail(PA_ERR_OOM, "pa_prefix_insert: host allocation failed");
@@ -379,18 +436,19 @@ pa_status pa_alloc_prompt_cached(pa_prefix_index* x, int64_t seq_id, const int32
   } catch (const std::bad_alloc&) {
     return pa::fail(PA_ERR_OOM, "pa_alloc_prompt_cached: host allocation failed");
   }
+  x->maybe_compact();
   return PA_OK;
 }
 
-pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out4) {
-  if (!x || !out4) return pa::fail(PA_ERR_INVALID, "pa_prefix_stats: NULL argument");
-  int64_t refs = 0, live = 0;
+pa_status pa_prefix_stats(const pa_prefix_index* x, int64_t* out5) {
+  if (!x || !out5) return pa::fail(PA_ERR_INVALID, "pa_prefix_stats: NULL argument");
+  int64_t refs = 0;
   for (const Entry& e : x->entries) refs += e.held;
-  for (const Node& nd : x->nodes) live += nd.alive ? 1 : 0;
-  out4[0] = int64_t(x->entries.size());
-  out4[1] = live;
-  out4[2] = refs;
-  out4[3] = x->evicted;
+  out5[0] = x->inserted;
+  out5[1] = x->live;
+  out5[2] = refs;
+  out5[3] = x->evicted;
+  out5[4] = int64_t(x->nodes.size());
   return PA_OK;
 }
 
@@ -426,6 +484,7 @@ pa_status pa_prefix_evict(pa_prefix_index* x, int64_t min_free_blocks, int64_t* 
   }
   x->evicted += n;
   if (num_evicted) *num_evicted = n;
+  x->maybe_compact();
   return PA_OK;
 }
 

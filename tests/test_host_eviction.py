@@ -183,3 +183,40 @@ def test_random_operations_match_the_oracle(bs, N, seed):
     ox.clear()
     _same(a, o, x, ox, [])
     assert a.num_free() == N
+
+
+def test_long_churn_keeps_memory_bounded():
+    """Thousands of requests through a small pool with eviction on: after every
+    step the C++ index equals the oracle tree (its evicted nodes and unused
+    entries are dropped and the rest renumbered in order along the way,
+    which must change nothing observable), and its node slots stay within
+    twice the live nodes plus the margin."""
+    rng = np.random.default_rng(77)
+    N, bs = 48, 4
+    order = rng.permutation(N)
+    a, o = pa.Allocator(N, bs, order), OracleAllocator(N, bs, order)
+    x, ox = pa.PrefixIndex(a, auto_evict=True), OracleRadixIndex(o, auto_evict=True)
+    bases = [[int(t) for t in rng.integers(0, 4, size=rng.integers(4, 30))] for _ in range(12)]
+    live, sid, peak = [], 0, 0
+    for step in range(3000):
+        if len(live) >= 3 or (live and rng.random() < 0.3):
+            s = live.pop(0)
+            toks = s[1]
+            assert x.insert(s[0], toks) == ox.insert(s[0], toks)
+            a.free_seq(s[0])
+            o.free_seq(s[0])
+        base = bases[rng.integers(0, len(bases))]
+        p = base[:rng.integers(1, len(base) + 1)] + [int(t) for t in rng.integers(0, 4, size=rng.integers(1, 12))]
+        got, want = _both(lambda: x.alloc_prompt_cached(sid, p), lambda: ox.alloc_prompt_cached(sid, p))
+        if want is not None:
+            assert got[0] == want[0] and list(got[1]) == want[1] and got[2] == want[2]
+            live.append((sid, p))
+        sid += 1
+        if step % 7 == 0:
+            m = int(rng.integers(0, N + 1))
+            assert x.evict(m) == ox.evict(m)
+        st = x.stats()
+        assert st["node_slots"] <= 2 * st["nodes"] + 65
+        peak = max(peak, st["node_slots"])
+        _same(a, o, x, ox, [s for s, _ in live])
+    assert ox.evicted > 500 and len(ox.nodes) > 4 * peak   # the oracle keeps every node ever made
