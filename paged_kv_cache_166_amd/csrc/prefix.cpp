@@ -373,7 +373,10 @@ pa_status pa_prefix_insert(pa_prefix_index* x, int64_t seq_id, const int32_t* to
       ++x->live;
     }
     for (int32_t b : e.refs) ++a->refs[b];
-    x->entries.push_back(std::move(e));
+    // An entry that adds no position (all of it already cached) creates no
+    // node and holds no reference: nothing will ever read it, so it is
+    // counted but not kept.
+    if (d < n) x->entries.push_back(std::move(e));
     ++x->inserted;
     if (divergence) *divergence = int32_t(d);
   } catch (const std::bad_alloc&) {
