@@ -324,7 +324,11 @@ pa_status pa_allocator_stats(const pa_allocator* a, int64_t* out5);
  * nodes point at the physical KV blocks; a new prompt reuses the blocks of
  * its longest cached prefix and only the rest is computed; an edge is split
  * where a new sequence leaves it).  Token ids are int32.  Not thread-safe;
- * destroy the index before its allocator.
+ * destroy the index before its allocator.  A host allocation failure inside
+ * an index call (PA_ERR_OOM with a "host allocation failed" message, as
+ * opposed to the allocator's block OOM, which changes nothing) may leave the
+ * index part-way through that call: clear it (pa_prefix_clear) before
+ * using it again.
  *
  * Blocks: an inserted sequence is an entry.  It provides the positions from
  * its divergence point d (its match length before insertion) to its end and
