@@ -478,13 +478,15 @@ __global__ __launch_bounds__(NW * 64) void decode_multi_kernel(DecodeMultiArgs m
 // M = max_p m_p, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
 // R threads per output element take every R-th partition with a running
 // maximum (all their loads can be in flight together), then combine in LDS.
-template <int D, int R>
-__global__ __launch_bounds__(D * R) void decode_merge_kernel(DecodeArgs a) {
+// A workgroup covers DC of the D output elements (blockIdx.z picks which):
+// many partitions take more threads per element and so more workgroups.
+template <int D, int R, int DC>
+__global__ __launch_bounds__(DC * R) void decode_merge_kernel(DecodeArgs a) {
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
   const int H = a.num_heads;
-  const int d = threadIdx.x % D;
-  const int r = threadIdx.x / D;
+  const int d = int(blockIdx.z) * DC + int(threadIdx.x) % DC;
+  const int r = threadIdx.x / DC;
   const int64_t sh = int64_t(seq) * H + head;
   const float* ml = a.ws_ml + 2 * sh * a.max_parts;
   const float* pa = a.ws_acc + sh * a.max_parts * D + d;
@@ -517,26 +519,42 @@ __global__ __launch_bounds__(D * R) void decode_merge_kernel(DecodeArgs a) {
     A = A * fo + x * fn;
     M = Mn;
   }
-  __shared__ float sm_a[R][D], sm_m[R][D], sm_s[R][D];
-  sm_a[r][d] = A;
-  sm_m[r][d] = M;
-  sm_s[r][d] = S;
+  const int dl = int(threadIdx.x) % DC;
+  __shared__ float sm_a[R][DC], sm_m[R][DC], sm_s[R][DC];
+  sm_a[r][dl] = A;
+  sm_m[r][dl] = M;
+  sm_s[r][dl] = S;
   __syncthreads();
   if (r != 0) return;
   float Mg = kNoMax;
 #pragma unroll
-  for (int i = 0; i < R; ++i) Mg = fmaxf(Mg, sm_m[i][d]);
+  for (int i = 0; i < R; ++i) Mg = fmaxf(Mg, sm_m[i][dl]);
   float Ag = 0.f, Sg = 0.f;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const float f = fast_exp2(sm_m[i][d] - Mg);
-    Ag = fmaf(sm_a[i][d], f, Ag);
-    Sg = fmaf(sm_s[i][d], f, Sg);
+    const float f = fast_exp2(sm_m[i][dl] - Mg);
+    Ag = fmaf(sm_a[i][dl], f, Ag);
+    Sg = fmaf(sm_s[i][dl], f, Sg);
   }
   store_from_f32(a.out, sh * D + d, a.out_dtype, Sg > 0.f ? Ag / Sg : 0.f);
 }
 
 constexpr int kWaves = 4;
+
+// The merge launch: up to 16 partitions, 512 / D threads per element over
+// all D elements in one workgroup; more, 16 threads per element over 64
+// elements per workgroup.
+template <int D>
+void launch_merge(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
+  if (a.max_parts <= 16) {
+    constexpr int R = 512 / D;
+    hipLaunchKernelGGL((decode_merge_kernel<D, R, D>), dim3(a.num_heads, num_seqs), dim3(D * R),
+                       0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_merge_kernel<D, 16, 64>), dim3(a.num_heads, num_seqs, D / 64),
+                       dim3(64 * 16), 0, stream, a);
+  }
+}
 
 template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_t stream) {
@@ -559,10 +577,7 @@ hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_
     hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, false>), grid, dim3(kWaves * 64),
                        0, stream, a);
   }
-  constexpr int R = 512 / D;
-  if (a.max_parts > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<D, R>), dim3(a.num_heads, num_seqs), dim3(D * R), 0,
-                       stream, a);
+  if (a.max_parts > 1) launch_merge<D>(a, num_seqs, stream);
   return hipGetLastError();
 }
 
@@ -602,9 +617,7 @@ hipError_t launch_multi_t(const DecodeMultiArgs& m, bool stream_v, int num_seqs,
     DecodeArgs a = m.base;
     a.block_size = 1;
     a.part_blocks = m.part_tokens;
-    constexpr int R = 512 / D;
-    hipLaunchKernelGGL((decode_merge_kernel<D, R>), dim3(a.num_heads, num_seqs), dim3(D * R), 0,
-                       stream, a);
+    launch_merge<D>(a, num_seqs, stream);
   }
   return hipGetLastError();
 }
