@@ -654,6 +654,7 @@ class DecodeBench:
         pairs = [(i, h) for h in range(self.H) for i in range(self.B)]
         done_bytes, n, spent = 0, 0, 0.0
         cache = {}
+        c0, w0 = time.process_time(), time.perf_counter()
         while spent < budget_s:
             i, h = pairs[n % len(pairs)]
             L = self.lens0[i] - 1
@@ -677,7 +678,9 @@ class DecodeBench:
             spent += time.perf_counter() - t0
             done_bytes += 2 * L * self.D * ELEM[self.kv]
             n += 1
-        return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": _cores(),
+        used = _cores_used(time.process_time() - c0, time.perf_counter() - w0)
+        return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": used,
+                "cores_available": _cores(),
                 "kind": "oracle",
                 "sample": f"{n} (sequence, head) decodes cycling over this workload's "
                           f"{len(pairs)} pairs at the prompt lengths, {spent:.1f} s of oracle "
@@ -767,6 +770,7 @@ class PrefillBench:
         from oracle import attention as A
         rng = np.random.default_rng(0)
         t0 = time.perf_counter()
+        c0 = time.process_time()
         flops = 0.0
         i = 0
         while time.perf_counter() - t0 < budget_s:
@@ -778,7 +782,9 @@ class PrefillBench:
             flops += 4.0 * self.D * (self.S * (L - self.S) + self.S * (self.S + 1) // 2)
             i += 1
         dt = time.perf_counter() - t0
-        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _cores(), "kind": "oracle",
+        used = _cores_used(time.process_time() - c0, dt)
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used,
+                "cores_available": _cores(), "kind": "oracle",
                 "sample": f"{i} (sequence, head) chunk attentions of this workload, {dt:.1f} s, "
                           "float64 NumPy"}
 
@@ -790,6 +796,12 @@ def _bits(t):
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)
     return t.view(torch.uint8).numpy()
+
+
+def _cores_used(cpu_s, wall_s):
+    """Threads the baseline kept busy on average: process CPU time (all
+    threads) over wall time."""
+    return round(cpu_s / wall_s, 2) if wall_s > 0 else None
 
 
 def _cores():
