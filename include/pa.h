@@ -203,6 +203,37 @@ pa_status pa_decode_append(void* out, int32_t out_dtype, const void* q, int32_t 
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_shared_prefix -- pa_decode of a batch whose sequences all begin
+ * with the same physical blocks (prefix sharing by copy-on-write, the
+ * DataWhale notes' section 4): the shared prefix is read once for the whole
+ * batch instead of once per sequence.  Same result as pa_decode up to the
+ * order of the floating-point sums (the same tolerance applies).
+ *   1. every sequence's query against the prefix keys, as a multi-query
+ *      pass on MFMA (the prefill kernel's tiles, no mask), chunk by chunk,
+ *      each chunk's (max, sum, unnormalised output) into the workspace;
+ *   2. each sequence's own blocks after the prefix, split into partitions of
+ *      partition_blocks (0: automatic) as in pa_decode, into the workspace;
+ *   3. the merge of all of them.
+ *   shared_blocks  the first shared_blocks entries of every row of
+ *                 block_tables are the same blocks, and every sequence's
+ *                 context covers them (context_lens[i] >= shared_blocks *
+ *                 block_size); 1 <= shared_blocks <= max_blocks_per_seq.  Not
+ *                 checked on the device.
+ * f16 and bf16 pools only (PA_ERR_UNSUPPORTED otherwise); q of the pool's
+ * type.  A workspace is always needed:
+ * pa_decode_shared_prefix_workspace_bytes(...).  Other arguments as pa_decode.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                               int32_t max_blocks_per_seq, int32_t shared_blocks,
+                                               int32_t partition_blocks);
+pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                  const pa_pool* pool, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t shared_blocks, float scale,
+                                  int32_t partition_blocks, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pa_decode_multi -- pa_decode of one batch whose sequences live in several
  * pools with the same num_heads, head_dim and kv_dtype (typically the
  * block-size views of one arena, pa_buddy_*), in one launch (plus the merge

@@ -39,6 +39,7 @@ EXPORTS = [
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_auto_partition_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_chunk",
     "pa_decode_multi_workspace_bytes", "pa_decode_multi", "pa_decode_append",
+    "pa_decode_shared_prefix_workspace_bytes", "pa_decode_shared_prefix",
     "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_prompt", "pa_append_tokens",
     "pa_append_tokens_batch", "pa_fork", "pa_free_seq", "pa_get_block_table",
     "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
@@ -81,6 +82,9 @@ def _load():
         "pa_decode_append": (I32, [VP, I32, VP, I32, P, VP, VP, VP, VP, I32, VP, I32,
                                    ctypes.c_float, I32, VP, SZ, VP]),
         "pa_decode_multi_workspace_bytes": (SZ, [P, pi32, I32, I32, I32]),
+        "pa_decode_shared_prefix_workspace_bytes": (SZ, [P, I32, I32, I32, I32]),
+        "pa_decode_shared_prefix": (I32, [VP, I32, VP, I32, P, VP, I32, VP, I32, I32,
+                                          ctypes.c_float, I32, VP, SZ, VP]),
         "pa_decode_multi": (I32, [VP, I32, VP, I32, P, I32, VP, pi32, pi32, VP, ctypes.c_float, I32,
                                   VP, SZ, VP]),
         "pa_prefill_chunk": (I32, [VP, I32, VP, I32, P, VP, I32, VP, VP, I32, I32, ctypes.c_float,
@@ -314,6 +318,43 @@ def pa_decode_append(out, q, pool, key_new, value_new, new_slots, block_tables, 
                                 maxb, _ptr(context_lens), B, float(scale), int(partition_blocks),
                                 _ptr(workspace), ws_bytes, _stream(stream, pool.device)),
            "pa_decode_append")
+
+
+def shared_prefix_workspace(pool, num_seqs, max_blocks_per_seq, shared_blocks,
+                            partition_blocks=0):
+    """A workspace tensor for pa_decode_shared_prefix."""
+    n = lib.pa_decode_shared_prefix_workspace_bytes(pool.ref(), num_seqs, max_blocks_per_seq,
+                                                    shared_blocks, partition_blocks)
+    if n == 0:
+        raise ValueError("pa_decode_shared_prefix_workspace_bytes: bad arguments")
+    return torch.empty(n, dtype=torch.uint8, device=pool.device)
+
+
+def shared_prefix_blocks(tables, lens, block_size):
+    """Leading blocks shared by every row of host tables [B, max_blocks] and
+    fully covered by every length (what pa_decode_shared_prefix may take)."""
+    import numpy as np
+    t = np.asarray(tables)
+    n = min(int(np.min(lens)) // block_size, t.shape[1])
+    same = np.all(t[:, :n] == t[:1, :n], axis=0)
+    return int(n if same.all() else np.argmin(same))
+
+
+def pa_decode_shared_prefix(out, q, pool, block_tables, context_lens, shared_blocks, scale,
+                            partition_blocks=0, workspace=None, stream=None):
+    """pa_decode with the first shared_blocks blocks of every table shared:
+    the prefix is attended once for the whole batch (on MFMA)."""
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    for t in (block_tables, q, out):
+        assert t.is_contiguous()
+    B, maxb = block_tables.shape
+    if workspace is None:
+        workspace = shared_prefix_workspace(pool, B, maxb, shared_blocks, partition_blocks)
+    _check(lib.pa_decode_shared_prefix(_ptr(out), dtype_code(out), _ptr(q), dtype_code(q),
+                                       pool.ref(), _ptr(block_tables), maxb, _ptr(context_lens), B,
+                                       int(shared_blocks), float(scale), int(partition_blocks),
+                                       _ptr(workspace), workspace.numel(),
+                                       _stream(stream, pool.device)), "pa_decode_shared_prefix")
 
 
 def _pool_array(pools):

@@ -72,6 +72,25 @@ WsLayout ws_layout_parts(const pa_pool* p, int32_t num_seqs, int32_t parts) {
   return w;
 }
 
+// The shared-prefix decode's geometry: prefix chunks (whole 32-key tiles,
+// at least 128 keys, at most about 64 chunks) and suffix partitions.
+struct PrefixPlan {
+  int32_t prefix_len, chunk_keys, chunks, suffix_pb, suffix_parts, total_parts;
+};
+
+PrefixPlan prefix_plan(const pa_pool* p, int32_t max_blocks, int32_t shared_blocks,
+                       int32_t partition_blocks) {
+  PrefixPlan g{};
+  g.prefix_len = shared_blocks * p->block_size;
+  const int32_t want = (g.prefix_len + 63) / 64;
+  g.chunk_keys = std::max<int32_t>(128, (want + 31) / 32 * 32);
+  g.chunks = (g.prefix_len + g.chunk_keys - 1) / g.chunk_keys;
+  g.suffix_pb = partition_blocks > 0 ? partition_blocks : auto_partition_blocks(p);
+  g.suffix_parts = (max_blocks - shared_blocks + g.suffix_pb - 1) / g.suffix_pb;
+  g.total_parts = g.chunks + g.suffix_parts;
+  return g;
+}
+
 WsLayout ws_layout(const pa_pool* p, int32_t num_seqs, int32_t max_blocks, int32_t part_blocks) {
   return ws_layout_parts(p, num_seqs, (max_blocks + part_blocks - 1) / part_blocks);
 }
@@ -219,6 +238,7 @@ pa_status decode_impl(const char* fn, void* out, int32_t out_dtype, const void* 
   a.block_size = pool->block_size;
   a.part_blocks = pb;
   a.max_parts = w.parts < 1 ? 1 : w.parts;
+  a.ws_parts = a.max_parts;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
@@ -262,6 +282,105 @@ pa_status pa_decode_append(void* out, int32_t out_dtype, const void* q, int32_t 
   return decode_impl("pa_decode_append", out, out_dtype, q, q_dtype, pool, key_new, value_new,
                      new_slots, block_tables, max_blocks_per_seq, context_lens, num_seqs, scale,
                      partition_blocks, workspace, workspace_bytes, stream);
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                               int32_t max_blocks_per_seq, int32_t shared_blocks,
+                                               int32_t partition_blocks) {
+  if (check_pool("pa_decode_shared_prefix_workspace_bytes", pool)) return 0;
+  if (num_seqs <= 0 || shared_blocks <= 0 || shared_blocks > max_blocks_per_seq ||
+      partition_blocks < 0 || partition_blocks > 256)
+    return 0;
+  const PrefixPlan g = prefix_plan(pool, max_blocks_per_seq, shared_blocks, partition_blocks);
+  // always a workspace: the prefix's partials are merged even alone
+  return size_t(ws_layout_parts(pool, num_seqs, std::max(g.total_parts, 2)).bytes);
+}
+
+pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                  const pa_pool* pool, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t shared_blocks, float scale,
+                                  int32_t partition_blocks, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "pa_decode_shared_prefix";
+  if (pa_status st = check_pool(fn, pool)) return st;
+  if (pool->kv_dtype != PA_F16 && pool->kv_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: f16 or bf16 pools (the prefix pass runs on MFMA)", fn);
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "%s: num_seqs %d", fn, num_seqs);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(q, 16) || !aligned(out, 16))
+    return fail(PA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
+  if (q_dtype != pool->kv_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype %d must equal kv_dtype %d", fn, q_dtype,
+                pool->kv_dtype);
+  if (out_dtype != PA_F32 && out_dtype != q_dtype)
+    return fail(PA_ERR_INVALID, "%s: out_dtype must be f32 or q_dtype", fn);
+  if (shared_blocks <= 0 || shared_blocks > max_blocks_per_seq)
+    return fail(PA_ERR_INVALID, "%s: shared_blocks %d (1..max_blocks_per_seq %d)", fn,
+                shared_blocks, max_blocks_per_seq);
+  if (partition_blocks < 0 || partition_blocks > 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: partition_blocks %d (1..256, or 0 = auto)", fn,
+                partition_blocks);
+  const PrefixPlan g = prefix_plan(pool, max_blocks_per_seq, shared_blocks, partition_blocks);
+  const WsLayout w = ws_layout_parts(pool, num_seqs, std::max(g.total_parts, 2));
+  if (!workspace || size_t(w.bytes) > workspace_bytes || !aligned(workspace, 256))
+    return fail(PA_ERR_INVALID, "%s: workspace of %lld bytes, 256-byte aligned, is required", fn,
+                (long long)w.bytes);
+  char* ws = static_cast<char*>(workspace);
+  float* ws_ml = reinterpret_cast<float*>(ws + w.ml_off);
+  float* ws_acc = reinterpret_cast<float*>(ws + w.acc_off);
+  const float scale_log2 = scale * 1.4426950408889634f;
+
+  // 1. the shared prefix: every sequence's query against the prefix keys,
+  //    chunk by chunk, into partitions 0 .. chunks-1
+  pa::PrefillArgs pf{};
+  pf.q = q;
+  pf.k_cache = pool->k_cache;
+  pf.v_cache = pool->v_cache;
+  pf.block_tables = block_tables;  // sequence 0's row holds the prefix
+  pf.max_blocks_per_seq = max_blocks_per_seq;
+  pf.num_heads = pool->num_heads;
+  pf.num_seqs = num_seqs;
+  pf.scale_log2 = scale_log2;
+  pf.out_dtype = out_dtype;
+  pf.ws_acc = ws_acc;
+  pf.ws_ml = ws_ml;
+  pf.max_parts = w.parts;
+  pf.prefix_len = g.prefix_len;
+  pf.chunk_keys = g.chunk_keys;
+  if (pa_status st = hip_status(fn, pa::launch_prefix_partials(pf, pool->kv_dtype, pool->head_dim,
+                                                               pool->block_size, stream)))
+    return st;
+
+  // 2. each sequence's own blocks after the prefix, into the partitions
+  //    after those, then 3. the merge of all of them
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_ml = ws_ml;
+  a.ws_acc = ws_acc;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = pool->num_heads;
+  a.block_size = pool->block_size;
+  a.part_blocks = g.suffix_pb;
+  a.max_parts = std::max(g.suffix_parts, 1);
+  a.first_block = shared_blocks;
+  a.prefix_parts = g.chunks;
+  a.ws_parts = w.parts;
+  a.scale_log2 = scale_log2;
+  a.q_dtype = q_dtype;
+  a.out_dtype = out_dtype;
+  return hip_status(fn, pa::launch_decode(a, pool->kv_dtype, pool->head_dim, pool->block_size,
+                                          (pool->flags & PA_POOL_STREAM_KV) != 0, num_seqs,
+                                          stream));
 }
 
 size_t pa_decode_multi_workspace_bytes(const pa_pool* pools, const int32_t* max_blocks_per_seq,
@@ -326,6 +445,7 @@ pa_status pa_decode_multi(void* out, int32_t out_dtype, const void* q, int32_t q
   a.ws_acc = w.parts > 1 ? reinterpret_cast<float*>(ws + w.acc_off) : nullptr;
   a.num_heads = p0->num_heads;
   a.max_parts = w.parts < 1 ? 1 : w.parts;
+  a.ws_parts = a.max_parts;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;

@@ -221,7 +221,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // entry w + NW t of the partition (bounded by the table's row length; the
   // entries past the sequence's blocks are never used).
   const int64_t out_off = (int64_t(seq) * H + head) * D;
-  const int blk0 = part * a.part_blocks;
+  const int blk0 = a.first_block + part * a.part_blocks;
   const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq + blk0;
   const int t_idx = wave + NW * lane;
   const int tab = (t_idx < a.part_blocks && blk0 + t_idx < a.max_blocks_per_seq) ? table[t_idx] : 0;
@@ -237,7 +237,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     return;
   }
   const int nblocks = (L + BS - 1) / BS;
-  const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
+  const int nparts = nblocks > a.first_block
+                         ? (nblocks - a.first_block + a.part_blocks - 1) / a.part_blocks
+                         : 0;
   if (part >= nparts) return;
   const int nb = min(a.part_blocks, nblocks - blk0);
   const bool row_ok = !G::kIdleGroups || grp < BS;
@@ -422,13 +424,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     }
   }
 
-  if (nparts == 1) {
+  if (nparts == 1 && a.prefix_parts == 0) {
     if (tid < D) store_from_f32(a.out, out_off + tid, a.out_dtype, S > 0.f ? A / S : 0.f);
     return;
   }
 
   // Split-K: publish this partition's (max, sum, acc) for the merge kernel.
-  const int64_t pidx = (int64_t(seq) * H + head) * a.max_parts + part;
+  const int64_t pidx = (int64_t(seq) * H + head) * a.ws_parts + a.prefix_parts + part;
   if (tid < D) a.ws_acc[pidx * D + tid] = A;
   if (tid == 0) {
     a.ws_ml[2 * pidx] = M;
@@ -488,22 +490,25 @@ __global__ __launch_bounds__(DC * R) void decode_merge_kernel(DecodeArgs a) {
   const int d = int(blockIdx.z) * DC + int(threadIdx.x) % DC;
   const int r = threadIdx.x / DC;
   const int64_t sh = int64_t(seq) * H + head;
-  const float* ml = a.ws_ml + 2 * sh * a.max_parts;
-  const float* pa = a.ws_acc + sh * a.max_parts * D + d;
+  const float* ml = a.ws_ml + 2 * sh * a.ws_parts;
+  const float* pa = a.ws_acc + sh * a.ws_parts * D + d;
   // Partition r's triple is loaded before the context length is known (it
-  // lies inside the workspace whenever r < max_parts, and is used only if
+  // lies inside the workspace whenever r < ws_parts, and is used only if
   // the partition exists), so the common case of at most R partitions waits
   // for one round trip to memory, not two.
   float m0 = kNoMax, l0 = 0.f, x0 = 0.f;
-  if (r < a.max_parts) {
+  if (r < a.ws_parts) {
     m0 = ml[2 * r];
     l0 = ml[2 * r + 1];
     x0 = pa[int64_t(r) * D];
   }
   const int L = a.context_lens[seq];
   const int nblocks = (L + a.block_size - 1) / a.block_size;
-  const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
-  if (nparts <= 1) return;
+  const int nparts = a.prefix_parts + (nblocks > a.first_block
+                                           ? (nblocks - a.first_block + a.part_blocks - 1) /
+                                                 a.part_blocks
+                                           : 0);
+  if (nparts <= 1 && a.prefix_parts == 0) return;
   float M = kNoMax, A = 0.f, S = 0.f;
   if (r < nparts) {
     M = m0;
@@ -546,7 +551,7 @@ constexpr int kWaves = 4;
 // elements per workgroup.
 template <int D>
 void launch_merge(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
-  if (a.max_parts <= 16) {
+  if (a.ws_parts <= 16) {
     constexpr int R = 512 / D;
     hipLaunchKernelGGL((decode_merge_kernel<D, R, D>), dim3(a.num_heads, num_seqs), dim3(D * R),
                        0, stream, a);
@@ -577,7 +582,7 @@ hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_
     hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, false>), grid, dim3(kWaves * 64),
                        0, stream, a);
   }
-  if (a.max_parts > 1) launch_merge<D>(a, num_seqs, stream);
+  if (a.max_parts > 1 || a.prefix_parts > 0) launch_merge<D>(a, num_seqs, stream);
   return hipGetLastError();
 }
 

@@ -31,6 +31,15 @@ struct DecodeArgs {
   const void* k_new;
   const void* v_new;
   const int64_t* new_slots;
+  // pa_decode_shared_prefix only (else 0): the first first_block blocks of
+  // every table are the shared prefix, attended elsewhere into partitions
+  // 0 .. prefix_parts-1; this launch covers the blocks after them, into
+  // partitions prefix_parts onwards.
+  int32_t first_block;
+  int32_t prefix_parts;
+  // partitions per (sequence, head) in the workspace (its stride): max_parts,
+  // or more when other launches own some of them (prefix_parts)
+  int32_t ws_parts;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,
@@ -106,9 +115,20 @@ struct PrefillArgs {
   int32_t num_seqs;
   float scale_log2;
   int32_t out_dtype;
+  // Shared-prefix partials (pa_decode_shared_prefix) only: every query row
+  // is one sequence's decode query; keys are the first prefix_len tokens of
+  // sequence 0's table, in chunks of chunk_keys; each chunk's (max, sum,
+  // unnormalised output) goes to partition `chunk` of the decode workspace.
+  float* ws_acc;
+  float* ws_ml;
+  int32_t max_parts;
+  int32_t prefix_len;
+  int32_t chunk_keys;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int block_size,
                           int max_query_len, hipStream_t stream);
+hipError_t launch_prefix_partials(const PrefillArgs& a, int kv_dtype, int head_dim,
+                                  int block_size, hipStream_t stream);
 
 }  // namespace pa

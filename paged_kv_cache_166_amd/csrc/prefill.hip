@@ -178,7 +178,12 @@ __device__ __forceinline__ void load_lds16(const void* src, char* dst) {
 // CU hides more of it than the registers the compiler gives up cost.  (fp16
 // with 4-token blocks, whose tile loads span two blocks, would spill at that
 // bound and keeps two.)
-template <int KV, int D, int BS>
+// kPrefix: the shared-prefix partials of pa_decode_shared_prefix -- query
+// rows are the batch's decode queries (row r = sequence r), keys are one
+// chunk of the shared prefix (sequence 0's table), no causal mask, and the
+// workgroup writes (max, sum, unnormalised output) per row to the decode
+// workspace instead of the normalised output.
+template <int KV, int D, int BS, bool kPrefix = false>
 __global__ __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(KV == PA_F16 && D == 128 && BS == 4 ? 2 : 3)))
 void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
@@ -230,16 +235,19 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   const int pair = xcd + kXcds * (g / num_qtiles);
   if (pair >= num_pairs) return;
   const int qtile = num_qtiles - 1 - (g % num_qtiles);
-  const int seq = pair / a.num_heads;
-  const int head = pair % a.num_heads;
   const int H = a.num_heads;
-
-  const int qs = a.query_start_loc[seq];
-  const int S = a.query_start_loc[seq + 1] - qs;
+  const int head = pair % H;
+  // kPrefix: pair = (chunk, head); keys [k0, L) of the prefix
+  const int chunk = kPrefix ? pair / H : 0;
+  const int seq = kPrefix ? 0 : pair / H;
+  const int qs = kPrefix ? 0 : a.query_start_loc[seq];
+  const int S = kPrefix ? a.num_seqs : a.query_start_loc[seq + 1] - qs;
   const int q_begin = qtile * kBM;
   if (q_begin >= S) return;
-  const int L = a.context_lens[seq];
-  const int ctx = L - S;  // tokens before the chunk
+  const int k0 = kPrefix ? chunk * a.chunk_keys : 0;
+  const int L = kPrefix ? min(k0 + a.chunk_keys, a.prefix_len) : a.context_lens[seq];
+  const int ctx = kPrefix ? 0 : L - S;  // tokens before the chunk
+  const int t0 = k0 / kBN;              // first tile (chunks are whole tiles)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -250,9 +258,9 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // This wave's query rows and the last key any of the workgroup's rows sees.
   const int wq0 = q_begin + wave * kQW;
   const int wg_last_row = min(q_begin + kBM, S) - 1;
-  const int n_keys = ctx + wg_last_row + 1;
-  const int n_tiles = (n_keys + kBN - 1) / kBN;
-  const int wave_last_key = wq0 < S ? ctx + min(wq0 + kQW, S) - 1 : -1;
+  const int n_keys = kPrefix ? L : ctx + wg_last_row + 1;
+  const int n_tiles = (n_keys + kBN - 1) / kBN - t0;
+  const int wave_last_key = wq0 < S ? (kPrefix ? L - 1 : ctx + min(wq0 + kQW, S) - 1) : -1;
 
   // Q^T fragments: lane holds query wq0 + col, dims kk*16 + 8*half .. +8.
   uint4 qf[kKSteps];
@@ -296,7 +304,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
 
   // DMA of tile t into K stage dk and V stage dv.
   auto dma_tile = [&](int t, char* dk, char* dv) {
-    const int kb = t * kBN;
+    const int kb = (t0 + t) * kBN;
     if (kBlocksPerLoad == 1 && kb + kBN <= L) {
       // Whole tile inside the sequence: one block per wave-load, uniform base.
       const int64_t in_blk = BS > kBN ? int64_t(kb % BS) * kRowBytes : 0;
@@ -372,7 +380,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
   float m = kNoMax, l = 0.f;
   const int my_row = wq0 + col;           // query row of this lane's column
-  const int my_lim = ctx + my_row;        // last key it sees
+  const int my_lim = kPrefix ? L - 1 : ctx + my_row;   // last key it sees
+  const int tile_lim = kPrefix ? L - 1 : ctx + wq0;    // last key every row of the wave sees
 
   // Prologue: tiles 0 and 1 in flight (past the last tile, the last again).
   using S0 = std::integral_constant<int, 0>;
@@ -392,7 +401,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     constexpr int s0 = decltype(st)::value;
     using Sn = std::integral_constant<int, (s0 + 1) % 3>;
     using Snn = std::integral_constant<int, (s0 + 2) % 3>;
-    const int kb = t * kBN;
+    const int kb = (t0 + t) * kBN;
     const bool active = kb <= wave_last_key;
     const char* kl = stage_k(st);
     auto kfrag = [&](int kk) {
@@ -425,7 +434,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       float x[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) x[v] = s[v];
-      if (kb + kBN - 1 > ctx + wq0) {  // the tile crosses the causal diagonal
+      if (kb + kBN - 1 > tile_lim) {  // the tile crosses the causal diagonal (or the chunk end)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kb + 8 * (v / 4) + 4 * half + (v % 4);
@@ -518,6 +527,22 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // Normalise and store: lane holds query my_row, dims 8*(v/4) + 4*half + v%4.
   const float2 lp = half_pair(l);
   l = lp.x + lp.y;
+  if constexpr (kPrefix) {
+    // (max, sum, unnormalised output) of this chunk for sequence my_row
+    if (my_row < S && wq0 < S) {
+      const int64_t pidx = (int64_t(my_row) * H + head) * a.max_parts + chunk;
+      if (half == 0) {
+        a.ws_ml[2 * pidx] = m;
+        a.ws_ml[2 * pidx + 1] = l;
+      }
+      float* acc = a.ws_acc + pidx * D;
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db * 32 + 8 * (v / 4) + 4 * half + (v % 4)] = o[db][v];
+    }
+    return;
+  }
   if (my_row < S && wq0 < S) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t ob = (int64_t(qs + my_row) * H + head) * D;
@@ -555,6 +580,38 @@ hipError_t launch_bs(const PrefillArgs& a, int bs, int mq, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+template <int KV, int D, int BS>
+hipError_t launch_prefix_t(const PrefillArgs& a, hipStream_t stream) {
+  const int num_qtiles = (a.num_seqs + kBM - 1) / kBM;
+  const int chunks = (a.prefix_len + a.chunk_keys - 1) / a.chunk_keys;
+  const int num_pairs = chunks * a.num_heads;
+  const int padded_pairs = (num_pairs + kXcds - 1) / kXcds * kXcds;
+  const int64_t blocks = int64_t(padded_pairs) * num_qtiles;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<KV, D, BS, true>), dim3(unsigned(blocks)), dim3(kWaves * 64),
+                     0, stream, a, num_qtiles, num_pairs);
+  return hipGetLastError();
+}
+
+template <int KV, int D>
+hipError_t launch_prefix_bs(const PrefillArgs& a, int bs, hipStream_t stream) {
+  switch (bs) {
+    case 4: return launch_prefix_t<KV, D, 4>(a, stream);
+    case 8: return launch_prefix_t<KV, D, 8>(a, stream);
+    case 16: return launch_prefix_t<KV, D, 16>(a, stream);
+    case 32: return launch_prefix_t<KV, D, 32>(a, stream);
+    case 64: return launch_prefix_t<KV, D, 64>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int KV>
+hipError_t launch_prefix_d(const PrefillArgs& a, int d, int bs, hipStream_t stream) {
+  if (d == 64) return launch_prefix_bs<KV, 64>(a, bs, stream);
+  if (d == 128) return launch_prefix_bs<KV, 128>(a, bs, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int KV>
 hipError_t launch_d(const PrefillArgs& a, int d, int bs, int mq, hipStream_t stream) {
   if (d == 64) return launch_bs<KV, 64>(a, bs, mq, stream);
@@ -568,6 +625,13 @@ hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int 
                           int max_query_len, hipStream_t stream) {
   if (kv_dtype == PA_BF16) return launch_d<PA_BF16>(a, head_dim, block_size, max_query_len, stream);
   if (kv_dtype == PA_F16) return launch_d<PA_F16>(a, head_dim, block_size, max_query_len, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefix_partials(const PrefillArgs& a, int kv_dtype, int head_dim,
+                                  int block_size, hipStream_t stream) {
+  if (kv_dtype == PA_BF16) return launch_prefix_d<PA_BF16>(a, head_dim, block_size, stream);
+  if (kv_dtype == PA_F16) return launch_prefix_d<PA_F16>(a, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,112 @@
+"""pa_decode_shared_prefix (the shared prefix attended once for the whole
+batch on MFMA, each sequence's own blocks by the decode kernel, then one
+merge) against the oracle and against pa_decode: block sizes, head sizes,
+both 16-bit types, prefixes of one block, of a length that is no multiple of
+the 32-key tile, and long enough to take wider chunks; batches of one and of
+more than one 128-row tile; sequences with no tokens after the prefix;
+several suffix partition sizes."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_166_amd as pa
+from tests.gpu_util import TOL, Scenario, assert_close, half_ulp
+from tests.test_gpu_decode import _oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch(kv, D, bs, H, shared_blocks, own, seed):
+    """Sequence 0 holds the prefix; the others fork it; then own tokens."""
+    N = shared_blocks + sum(-(-n // bs) for n in own) + len(own) + 4
+    sc = Scenario(N, H, bs, D, kv, seed=seed)
+    sc.prompt(0, shared_blocks * bs)
+    for i in range(1, len(own)):
+        sc.fork(0, i)
+    for i, n in enumerate(own):
+        if n:
+            assert sc.append(i, n) is None          # the prefix ends on a block boundary
+    return sc
+
+
+def _run(sc, seqs, q_dev, shared_blocks, scale, pb=0, out_dtype=torch.float32):
+    t_dev, ln_dev, t, ln = sc.device_tables(seqs)
+    assert pa.shared_prefix_blocks(t, ln, sc.bs) >= shared_blocks
+    out = torch.full(q_dev.shape, float("nan"), dtype=out_dtype, device="cuda")
+    pa.pa_decode_shared_prefix(out, q_dev, sc.pool, t_dev, ln_dev, shared_blocks, scale, pb)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [4, 16, 32, 64])
+def test_sweep(kv, D, bs):
+    H = 3
+    for shared_blocks, own in [(1, [0, 1, 5, 40]),
+                               (max(1, 100 // bs), [3, 0, 77, 200, 1]),
+                               (max(1, 600 // bs), [int(x) for x in np.arange(131) % 37])]:
+        sc = _batch(kv, D, bs, H, shared_blocks, own, seed=bs + D + shared_blocks)
+        seqs = list(range(len(own)))
+        q_dev, q64 = sc.random_q(len(seqs), kv)
+        scale = 1 / math.sqrt(D)
+        ref = _oracle(sc, seqs, q64, scale)
+        for pb in (0, 1, 3):
+            got = _run(sc, seqs, q_dev, shared_blocks, scale, pb)
+            assert_close(got, ref, TOL[kv], f"{kv} D={D} bs={bs} prefix={shared_blocks} pb={pb}")
+        got = _run(sc, seqs, q_dev, shared_blocks, scale, 0, out_dtype=pa.TORCH_DTYPE[kv])
+        assert np.all(np.abs(got - ref) <= TOL[kv] + half_ulp(kv, ref)), "low-precision output"
+
+
+def test_long_prefix_takes_wider_chunks():
+    """A 9600-token prefix (more than 64 chunks of 128 keys)."""
+    sc = _batch("bf16", 128, 64, 2, 150, [0, 9, 130, 64], seed=9)
+    seqs = [0, 1, 2, 3]
+    q_dev, q64 = sc.random_q(4, "bf16")
+    ref = _oracle(sc, seqs, q64, 0.1)
+    assert_close(_run(sc, seqs, q_dev, 150, 0.1), ref, TOL["bf16"], "long prefix")
+
+
+def test_prefix_cow_workload():
+    """The shared-prefix workload's decode step (64 sequences, 1024-token
+    prefix in 64 blocks of 16, 1..256 own tokens plus the step's, 40 heads x
+    128, bf16): every output against the oracle and against pa_decode."""
+    import workloads as W
+    cfg = W.CONFIGS["prefix_cow"]
+    own = [int(s) + 1 for s in W.uniform_ints(cfg["seed"], cfg["batch"], cfg["suffix_lo"],
+                                              cfg["suffix_hi"])]
+    sc = _batch("bf16", cfg["head_dim"], cfg["block_size"], cfg["num_heads"],
+                cfg["prefix"] // cfg["block_size"], own, seed=cfg["seed"])
+    seqs = list(range(cfg["batch"]))
+    q_dev, q64 = sc.random_q(len(seqs), "bf16")
+    scale = 1 / math.sqrt(cfg["head_dim"])
+    ref = _oracle(sc, seqs, q64, scale)
+    got = _run(sc, seqs, q_dev, cfg["prefix"] // cfg["block_size"], scale)
+    err = assert_close(got, ref, TOL["bf16"], "shared-prefix decode")
+    t_dev, ln_dev, _, _ = sc.device_tables(seqs)
+    plain = torch.empty(q_dev.shape, dtype=torch.float32, device="cuda")
+    pa.pa_decode(plain, q_dev, sc.pool, t_dev, ln_dev, scale, 0,
+                 pa.decode_workspace(sc.pool, len(seqs), t_dev.shape[1]))
+    torch.cuda.synchronize()
+    assert_close(got, plain.cpu().numpy().astype(np.float64), TOL["bf16"], "against pa_decode")
+    print(f"shared-prefix decode: max abs err {err:.2e}")
+
+
+def test_refusals():
+    sc = Scenario(8, 2, 16, 128, "fp8", seed=3)
+    sc.prompt(0, 32)
+    t_dev, ln_dev, _, _ = sc.device_tables([0])
+    q = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((1, 2, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    with pytest.raises(NotImplementedError):
+        pa.pa_decode_shared_prefix(out, q, sc.pool, t_dev, ln_dev, 1, 0.1, 0, ws)
+    sc2 = Scenario(8, 2, 16, 128, "bf16", seed=3)
+    sc2.prompt(0, 32)
+    t2, l2, _, _ = sc2.device_tables([0])
+    with pytest.raises(ValueError):
+        pa.pa_decode_shared_prefix(out, q, sc2.pool, t2, l2, 0, 0.1, 0, ws)   # no shared block
+    with pytest.raises(ValueError):
+        pa.pa_decode_shared_prefix(out, q, sc2.pool, t2, l2, 1, 0.1, 0, ws[:16])  # workspace
