@@ -605,6 +605,52 @@ class DecodeBench:
         t = float(np.median(ts))
         return {"us": t * 1e6, "bytes": 2 * 2 * tile, "GBps": 2 * 2 * tile / t / 1e9}
 
+    def shared_prefix_series(self, reps=20):
+        """The batch at its current lengths on the middle layer's pool, warm,
+        decoded two ways with the same inputs: pa_decode (every sequence
+        reads the shared prefix itself) and pa_decode_shared_prefix (the
+        prefix read once for the whole batch on MFMA, each sequence's own
+        blocks by the decode kernel, one merge).  Event-timed medians; GB/s
+        over the logical bytes (every sequence's full context) and over the
+        unique bytes (the prefix once)."""
+        lens = self.lens_now()
+        t, ln = self.alloc.pack(self.ids, self.maxb)
+        shared = pa.shared_prefix_blocks(t, ln, self.bs)
+        if shared == 0:
+            return None
+        pool = self.pools[len(self.pools) // 2]
+        td = torch.from_numpy(t).to(self.device)
+        lnd = torch.from_numpy(ln).to(self.device)
+        q = self.q[0]
+        out = torch.empty_like(q)
+        ws_sp = pa.shared_prefix_workspace(pool, self.B, self.maxb, shared, 0)
+
+        def timed(call):
+            ts = []
+            for r in range(reps + 3):
+                tm = Timer()
+                tm.start()
+                call()
+                tm.stop()
+                torch.cuda.synchronize()
+                if r >= 3:
+                    ts.append(tm.seconds())
+            return float(np.median(ts))
+
+        fused, self.fused = self.fused, False
+        logical = self.decode_bytes(lens)      # no new rows stored in these calls
+        self.fused = fused
+        unique = self.unique_bytes(lens)       # K/V rows, the prefix once
+        sec_d = timed(lambda: pa.pa_decode(out, q, pool, td, lnd, self.scale, self.pb, self.ws))
+        sec_s = timed(lambda: pa.pa_decode_shared_prefix(out, q, pool, td, lnd, shared, self.scale,
+                                                         0, ws_sp))
+        res = {"shared_blocks": shared, "logical_bytes": logical, "unique_bytes": unique}
+        for name, sec in (("pa_decode", sec_d), ("pa_decode_shared_prefix", sec_s)):
+            res[name] = {"us": sec * 1e6, "logical_GBps": logical / sec / 1e9,
+                         "unique_GBps": unique / sec / 1e9}
+        res["speedup"] = sec_d / sec_s
+        return res
+
     def lens_now(self):
         return np.array([self.alloc.seq_len(int(i)) for i in self.ids], dtype=np.int64)
 
@@ -916,6 +962,8 @@ def main():
             res["unique_bytes_per_launch"] = ub
             res["unique_GBps"] = ub / kt / 1e9
             res["cow_copy"] = b.cow_copy_us()
+            log("bench: shared-prefix decode")
+            res["shared_prefix_decode"] = b.shared_prefix_series()
             log("bench: prefix reuse")
             res["prefix_reuse"] = b.prefix_reuse()
             log("bench: eviction churn (host)")
