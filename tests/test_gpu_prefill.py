@@ -84,3 +84,36 @@ def test_chunked_prefill_workload():
                           heads=heads)
     err = assert_close(got[:, heads], ref[:, heads], TOL["bf16"], "chunked prefill")
     print(f"chunked prefill: ctx={ctx} max abs err {err:.2e}")
+
+
+def test_prefill_empty_chunks_and_no_op_calls():
+    """Sequences with no query rows in the batch (first, middle and last),
+    max_query_len above every chunk, and the calls that do nothing (no
+    sequences, max_query_len 0), which leave out untouched."""
+    ctx = [40, 7, 0, 300, 64, 33]
+    chunk = [0, 33, 1, 0, 130, 0]
+    bs = 16
+    N = sum(-(-(c + s) // bs) for c, s in zip(ctx, chunk)) + 4
+    sc = Scenario(N, 2, bs, 128, "f16", seed=47)
+    for i, (c, s) in enumerate(zip(ctx, chunk)):
+        sc.prompt(i, c)
+        if s:
+            sc.append(i, s)
+    seqs = list(range(len(ctx)))
+    qsl = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q_dev, q64 = sc.random_q(int(qsl[-1]), "f16")
+    scale = 1 / math.sqrt(128)
+    tables, lens = sc.oracle_tables(seqs)
+    ref = A.prefill_chunk(q64, qsl, sc.ok, sc.ov, "f16", tables, lens, bs, scale)
+    t_dev, ln_dev, _, _ = sc.device_tables(seqs)
+    qsl_dev = torch.from_numpy(qsl).cuda()
+    for mq in (130, 300):
+        out = torch.full(q_dev.shape, float("nan"), dtype=torch.float32, device="cuda")
+        pa.pa_prefill_chunk(out, q_dev, sc.pool, t_dev, ln_dev, qsl_dev, mq, scale)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy().astype(np.float64), ref, TOL["f16"], f"empty chunks mq={mq}")
+    out = torch.full(q_dev.shape, 7.0, dtype=torch.float32, device="cuda")
+    pa.pa_prefill_chunk(out, q_dev, sc.pool, t_dev[:0], ln_dev[:0], qsl_dev[:1], 130, scale)
+    pa.pa_prefill_chunk(out, q_dev, sc.pool, t_dev, ln_dev, qsl_dev, 0, scale)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
