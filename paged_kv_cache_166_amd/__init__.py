@@ -160,6 +160,30 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _on_device(what, device, *tensors):
+    """Every tensor of a GPU call lives on the pool's GPU and is contiguous:
+    the kernels take raw pointers, so a host tensor or a strided view would
+    be read as device memory of the wrong shape."""
+    if device.type != "cuda":
+        raise ValueError(f"{what}: the pool is on {device}, not on a GPU")
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: tensors must be contiguous")
+        if t.device != device:
+            raise ValueError(f"{what}: a tensor is on {t.device}, the pool on {device}")
+
+
+def _shape(what, name, t, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _ws_bytes(workspace):
+    return workspace.numel() * workspace.element_size() if workspace is not None else 0
+
+
 def dtype_code(x):
     if isinstance(x, str):
         return _NAME[x]
@@ -246,8 +270,13 @@ class PagedPool:
 
 def pa_reshape_and_cache(pool, key, value, slot_mapping, stream=None):
     """key/value [T, H, D] (contiguous), slot_mapping [T] int64 on the device."""
-    assert key.is_contiguous() and value.is_contiguous() and slot_mapping.dtype == torch.int64
+    what = "pa_reshape_and_cache"
+    assert slot_mapping.dtype == torch.int64
+    _on_device(what, pool.device, key, value, slot_mapping)
     T = key.shape[0]
+    for name, t in (("key", key), ("value", value)):
+        _shape(what, name, t, (T, pool.num_heads, pool.head_dim))
+    _shape(what, "slot_mapping", slot_mapping, (T,))
     _check(lib.pa_reshape_and_cache(pool.ref(), _ptr(key), _ptr(value), dtype_code(key),
                                     _ptr(slot_mapping), T, _stream(stream, pool.device)),
            "pa_reshape_and_cache")
@@ -255,7 +284,9 @@ def pa_reshape_and_cache(pool, key, value, slot_mapping, stream=None):
 
 def pa_copy_blocks(pool, src_dst, stream=None):
     """src_dst [n, 2] int32 on the device."""
-    assert src_dst.dtype == torch.int32 and src_dst.is_contiguous()
+    assert src_dst.dtype == torch.int32
+    _on_device("pa_copy_blocks", pool.device, src_dst)
+    _shape("pa_copy_blocks", "src_dst", src_dst, (src_dst.shape[0], 2))
     _check(lib.pa_copy_blocks(pool.ref(), _ptr(src_dst), src_dst.shape[0],
                               _stream(stream, pool.device)), "pa_copy_blocks")
 
@@ -280,9 +311,13 @@ def pa_decode(out, q, pool, block_tables, context_lens, scale, partition_blocks=
               workspace=None, stream=None, q_dtype=None, out_dtype=None):
     """out/q [B, H, D]; block_tables [B, max_blocks] int32; context_lens [B] int32."""
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
-    assert block_tables.is_contiguous() and q.is_contiguous() and out.is_contiguous()
+    what = "pa_decode"
+    _on_device(what, pool.device, out, q, block_tables, context_lens, workspace)
     B, maxb = block_tables.shape
-    ws_bytes = workspace.numel() if workspace is not None else 0
+    for name, t in (("q", q), ("out", out)):
+        _shape(what, name, t, (B, pool.num_heads, pool.head_dim))
+    _shape(what, "context_lens", context_lens, (B,))
+    ws_bytes = _ws_bytes(workspace)
     _check(lib.pa_decode(_ptr(out), dtype_code(out) if out_dtype is None else out_dtype,
                          _ptr(q), dtype_code(q) if q_dtype is None else q_dtype, pool.ref(),
                          _ptr(block_tables), maxb, _ptr(context_lens), B, float(scale),
@@ -295,7 +330,13 @@ def pa_prefill_chunk(out, q, pool, block_tables, context_lens, query_start_loc, 
     """out/q packed [T, H, D]; query_start_loc [B+1] int32; context_lens [B] int32."""
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     assert query_start_loc.dtype == torch.int32
+    what = "pa_prefill_chunk"
+    _on_device(what, pool.device, out, q, block_tables, context_lens, query_start_loc)
     B, maxb = block_tables.shape
+    _shape(what, "q", q, (q.shape[0], pool.num_heads, pool.head_dim))
+    _shape(what, "out", out, q.shape)
+    _shape(what, "context_lens", context_lens, (B,))
+    _shape(what, "query_start_loc", query_start_loc, (B + 1,))
     _check(lib.pa_prefill_chunk(_ptr(out), dtype_code(out), _ptr(q), dtype_code(q), pool.ref(),
                                 _ptr(block_tables), maxb, _ptr(context_lens),
                                 _ptr(query_start_loc), B, int(max_query_len), float(scale),
@@ -309,10 +350,15 @@ def pa_decode_append(out, q, pool, key_new, value_new, new_slots, block_tables, 
     [B, H, D] of the pool's type."""
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     assert new_slots.dtype == torch.int64 and key_new.dtype == value_new.dtype
-    for t in (block_tables, q, out, key_new, value_new, new_slots):
-        assert t.is_contiguous()
+    what = "pa_decode_append"
+    _on_device(what, pool.device, out, q, key_new, value_new, new_slots, block_tables,
+               context_lens, workspace)
     B, maxb = block_tables.shape
-    ws_bytes = workspace.numel() if workspace is not None else 0
+    for name, t in (("q", q), ("out", out), ("key_new", key_new), ("value_new", value_new)):
+        _shape(what, name, t, (B, pool.num_heads, pool.head_dim))
+    _shape(what, "new_slots", new_slots, (B,))
+    _shape(what, "context_lens", context_lens, (B,))
+    ws_bytes = _ws_bytes(workspace)
     _check(lib.pa_decode_append(_ptr(out), dtype_code(out), _ptr(q), dtype_code(q), pool.ref(),
                                 _ptr(key_new), _ptr(value_new), _ptr(new_slots), _ptr(block_tables),
                                 maxb, _ptr(context_lens), B, float(scale), int(partition_blocks),
@@ -345,15 +391,18 @@ def pa_decode_shared_prefix(out, q, pool, block_tables, context_lens, shared_blo
     """pa_decode with the first shared_blocks blocks of every table shared:
     the prefix is attended once for the whole batch (on MFMA)."""
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
-    for t in (block_tables, q, out):
-        assert t.is_contiguous()
+    what = "pa_decode_shared_prefix"
+    _on_device(what, pool.device, out, q, block_tables, context_lens, workspace)
     B, maxb = block_tables.shape
+    for name, t in (("q", q), ("out", out)):
+        _shape(what, name, t, (B, pool.num_heads, pool.head_dim))
+    _shape(what, "context_lens", context_lens, (B,))
     if workspace is None:
         workspace = shared_prefix_workspace(pool, B, maxb, shared_blocks, partition_blocks)
     _check(lib.pa_decode_shared_prefix(_ptr(out), dtype_code(out), _ptr(q), dtype_code(q),
                                        pool.ref(), _ptr(block_tables), maxb, _ptr(context_lens), B,
                                        int(shared_blocks), float(scale), int(partition_blocks),
-                                       _ptr(workspace), workspace.numel(),
+                                       _ptr(workspace), _ws_bytes(workspace),
                                        _stream(stream, pool.device)), "pa_decode_shared_prefix")
 
 
@@ -378,7 +427,20 @@ def pa_decode_multi(out, q, pools, block_tables, context_lens, seq_begin, scale,
     of out/q/context_lens use pools[g] and block_tables[g] ([rows, max_blocks_g]
     int32 on the device, or None for an empty group)."""
     assert len(pools) == len(block_tables) and len(seq_begin) == len(pools) + 1
-    assert q.is_contiguous() and out.is_contiguous() and context_lens.dtype == torch.int32
+    assert context_lens.dtype == torch.int32
+    what = "pa_decode_multi"
+    dev = pools[0].device
+    _on_device(what, dev, out, q, context_lens, workspace, *block_tables)
+    for p in pools:
+        _on_device(what, dev, p.k_cache, p.v_cache, p.k_scale, p.v_scale)
+    B = int(seq_begin[-1])
+    for name, t in (("q", q), ("out", out)):
+        _shape(what, name, t, (B, pools[0].num_heads, pools[0].head_dim))
+    _shape(what, "context_lens", context_lens, (B,))
+    for g, t in enumerate(block_tables):
+        rows = int(seq_begin[g + 1]) - int(seq_begin[g])
+        if t is not None and t.shape[0] != rows:
+            raise ValueError(f"{what}: block_tables[{g}] has {t.shape[0]} rows, the group {rows}")
     arr, parr = _pool_array(pools)
     G = len(pools)
     tabs = (ctypes.c_void_p * G)(*[t.data_ptr() if t is not None else 0 for t in block_tables])
@@ -386,7 +448,7 @@ def pa_decode_multi(out, q, pools, block_tables, context_lens, seq_begin, scale,
         assert t is None or (t.dtype == torch.int32 and t.is_contiguous() and t.dim() == 2)
     mb = (ctypes.c_int32 * G)(*[t.shape[1] if t is not None else 1 for t in block_tables])
     sb = (ctypes.c_int32 * (G + 1))(*[int(x) for x in seq_begin])
-    ws_bytes = workspace.numel() if workspace is not None else 0
+    ws_bytes = _ws_bytes(workspace)
     _check(lib.pa_decode_multi(_ptr(out), dtype_code(out), _ptr(q), dtype_code(q), parr, G,
                                ctypes.cast(tabs, ctypes.c_void_p), mb, sb, _ptr(context_lens),
                                float(scale), int(partition_tokens), _ptr(workspace), ws_bytes,

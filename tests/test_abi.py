@@ -137,3 +137,37 @@ def test_decode_multi_rejects_bad_arguments_before_launch():
                                                2, 64)
     assert n > 0
     assert call(pt=64) == pa.PA_ERR_INVALID                   # workspace missing
+
+
+def test_binding_refuses_host_tensors_and_wrong_shapes():
+    """The binding checks device, contiguity and shapes before any launch (the
+    kernels take raw pointers): host tensors, strided views and mis-shaped
+    operands raise ValueError without reaching the library."""
+    pool = pa.PagedPool.empty(8, 2, 16, 128, "f16", "cpu")
+    q = torch.zeros((3, 2, 128), dtype=torch.float16)
+    out = torch.zeros_like(q)
+    tables = torch.zeros((3, 4), dtype=torch.int32)
+    lens = torch.ones(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        pa.pa_decode(out, q, pool, tables, lens, 0.1)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        pa.pa_prefill_chunk(out, q, pool, tables, lens, torch.zeros(4, dtype=torch.int32), 1, 0.1)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        pa.pa_reshape_and_cache(pool, q, q, torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        pa.pa_copy_blocks(pool, torch.zeros((1, 2), dtype=torch.int32))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        pa.pa_decode_append(out, q, pool, q, q, torch.zeros(3, dtype=torch.int64), tables, lens,
+                            0.1)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        pa.pa_decode_shared_prefix(out, q, pool, tables, lens, 1, 0.1)
+    # the checks themselves, on the host device
+    dev = torch.device("cpu")
+    with pytest.raises(ValueError, match="contiguous"):
+        pa._on_device("f", torch.device("cuda:0"), torch.zeros((4, 4)).t())
+    with pytest.raises(ValueError, match="is on cpu"):
+        pa._on_device("f", torch.device("cuda:0"), torch.zeros(2))
+    with pytest.raises(ValueError, match="expected"):
+        pa._shape("f", "q", torch.zeros((3, 2, 64)), (3, 2, 128))
+    pa._shape("f", "q", q, (3, 2, 128))
+    assert dev.type == "cpu"
