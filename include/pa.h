@@ -168,7 +168,9 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
  *   partition_blocks  blocks per split-K partition, 1..256 (0 = automatic).
  *                 Sequences longer than one partition are split; the
  *                 partitions' (max, sum, output) triples are merged by a
- *                 second, small kernel on the same stream.
+ *                 second, small kernel on the same stream.  At most 65535
+ *                 partitions per sequence (ceil(max_blocks_per_seq /
+ *                 partition_blocks)); more is PA_ERR_UNSUPPORTED.
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 256-byte
  *                 aligned (may be NULL when that is 0).  Calls that share a
  *                 workspace must be ordered (same stream).

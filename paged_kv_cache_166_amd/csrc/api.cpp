@@ -47,6 +47,9 @@ pa_status hip_status(const char* fn, hipError_t e) {
   return PA_OK;
 }
 
+// Partitions per sequence are the launch grid's z dimension.
+constexpr int32_t kMaxParts = 65535;
+
 // 512 tokens per partition: long enough that a workgroup's fixed costs
 // (table and query loads, the final merge) are small next to its stream of
 // K/V, short enough that ragged batches still split into many workgroups.
@@ -115,6 +118,9 @@ pa_status check_multi(const char* fn, const pa_pool* pools, int32_t num_groups,
                   "%s: partition of %d tokens is not 1..256 blocks of %d", fn, part_tokens, bs);
     if (max_blocks[g] <= 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq <= 0", fn);
     const int64_t p = (int64_t(max_blocks[g]) * bs + part_tokens - 1) / part_tokens;
+    if (p > kMaxParts)
+      return fail(PA_ERR_UNSUPPORTED, "%s: %lld partitions per sequence (at most %d)", fn,
+                  (long long)p, kMaxParts);
     *parts = std::max<int32_t>(*parts, int32_t(p));
   }
   return PA_OK;
@@ -216,6 +222,9 @@ pa_status decode_impl(const char* fn, void* out, int32_t out_dtype, const void* 
                 partition_blocks);
   const int32_t pb = partition_blocks > 0 ? partition_blocks : auto_partition_blocks(pool);
   const WsLayout w = ws_layout(pool, num_seqs, max_blocks_per_seq, pb);
+  if (w.parts > kMaxParts)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d partitions per sequence (at most %d)", fn, w.parts,
+                kMaxParts);
   if (w.parts > 1) {
     if (!workspace || size_t(w.bytes) > workspace_bytes || !aligned(workspace, 256))
       return fail(PA_ERR_INVALID, "%s: workspace of %lld bytes, 256-byte aligned, is required",
@@ -324,6 +333,9 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
     return fail(PA_ERR_UNSUPPORTED, "%s: partition_blocks %d (1..256, or 0 = auto)", fn,
                 partition_blocks);
   const PrefixPlan g = prefix_plan(pool, max_blocks_per_seq, shared_blocks, partition_blocks);
+  if (g.total_parts > kMaxParts)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d partitions per sequence (at most %d)", fn,
+                g.total_parts, kMaxParts);
   const WsLayout w = ws_layout_parts(pool, num_seqs, std::max(g.total_parts, 2));
   if (!workspace || size_t(w.bytes) > workspace_bytes || !aligned(workspace, 256))
     return fail(PA_ERR_INVALID, "%s: workspace of %lld bytes, 256-byte aligned, is required", fn,

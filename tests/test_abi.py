@@ -171,3 +171,11 @@ def test_binding_refuses_host_tensors_and_wrong_shapes():
         pa._shape("f", "q", torch.zeros((3, 2, 64)), (3, 2, 128))
     pa._shape("f", "q", q, (3, 2, 128))
     assert dev.type == "cpu"
+
+
+def test_decode_refuses_more_partitions_than_the_grid_holds():
+    """ceil(max_blocks_per_seq / partition_blocks) partitions form the launch
+    grid's z dimension (at most 65535): more is refused before any launch."""
+    assert _decode(_fake_pool(), maxb=70000, pb=1) == pa.PA_ERR_UNSUPPORTED
+    assert b"partitions" in pa.lib.pa_last_error()
+    assert _decode(_fake_pool(), maxb=70000, pb=2) != pa.PA_ERR_UNSUPPORTED   # 35000 partitions
