@@ -22,10 +22,21 @@ What it computes, and where the pages define it:
 * ``attention`` -- textbook softmax attention in float64 over the gathered
   K/V, for one decode token per sequence and for a causal query chunk.
   (PagedAttention blog article, section 3.2.2 forward pass; course ch. 4.)
-* ``fp8`` -- the OCP FP8 E4M3FN codec written from the format definition.
+* ``fp8`` -- the OCP FP8 E4M3FN codec written from the format definition;
+  ``cache`` also holds the fp8 write with per-(block, head) scale upkeep
+  (the blog's mixed-precision KV storage).
+* ``prefix`` -- the prefix index over token ids as a flat list with
+  longest-common-prefix matching, bound to the allocator (study notes,
+  RadixAttention section and its exercise).
+* ``radix`` -- the same index as a radix tree, with least-recently-used
+  eviction of leaves when memory runs out (study notes, same section).
+* ``buddy`` -- a block size per request carved from one arena by a binary
+  buddy system (blog, "3.0" feature list: a page size fitted to the
+  request's length).
 
 Every function is written for readability, not speed.  Pins that tie each
 function to the pages or to mathematics live in ``tests/test_oracle_*.py``.
-The only part without a printed worked example is the attention arithmetic;
-it is pinned by closed forms, an independent library routine and brute force.
+The attention arithmetic has no printed worked example; it is pinned by
+closed forms, an independent library routine and brute force.  The eviction
+and buddy readings are pinned by hand-worked cases and invariants.
 """
