@@ -799,6 +799,46 @@ class PrefillBench:
     def kernel_spread(self):
         return spread([tm.seconds() for tm in self.ev])
 
+    def fp8_series(self, reps=20):
+        """The workload's launch over an fp8 E4M3 pool (codes drawn N(0, 40^2)
+        with scale 1/40 per (block, head), so values are N(0,1)) with the same
+        bf16 queries, tables and lengths: event-timed median, causal TFLOP/s,
+        and the K/V bytes (one byte per element)."""
+        N, H, D, bs = self.N, self.H, self.D, self.bs
+        pool = pa.PagedPool.empty(N, H, bs, D, "fp8", self.device)
+        g = torch.Generator(device=self.device)
+        g.manual_seed(5)
+        for t in (pool.k_cache, pool.v_cache):
+            for i in range(0, N, 1024):
+                n = min(1024, N - i)
+                x = torch.randn((n,) + tuple(t.shape[1:]), generator=g, device=self.device)
+                t[i:i + n] = (x * 40.0).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        pool.k_scale.fill_(1.0 / 40.0)
+        pool.v_scale.fill_(1.0 / 40.0)
+        ids = np.arange(self.next_id, self.next_id + self.B, dtype=np.int64)
+        self.next_id += self.B
+        for j, sid in enumerate(ids):
+            self.alloc.alloc_prompt(int(sid), self.ctx[j] + self.S)
+        t, ln = self.alloc.pack(ids, self.maxb)
+        td, ld = torch.from_numpy(t).to(self.device), torch.from_numpy(ln).to(self.device)
+        out = torch.empty_like(self.out)
+        ts = []
+        for r in range(reps + 3):
+            tm = Timer()
+            tm.start()
+            pa.pa_prefill_chunk(out, self.q, pool, td, ld, self.qsl, self.S, self.scale)
+            tm.stop()
+            torch.cuda.synchronize()
+            if r >= 3:
+                ts.append(tm.seconds())
+        for sid in ids:
+            self.alloc.free_seq(int(sid))
+        sec = float(np.median(ts))
+        del pool
+        return {"kv_dtype": "fp8", "q_dtype": "bf16", "us": sec * 1e6,
+                "TFLOPs": self.flops() / sec / 1e12,
+                "kv_bytes": 2 * H * D * sum(c + self.S for c in self.ctx)}
+
     def hbm_bytes(self):
         """Algorithmic bytes of one launch: every context and chunk K/V row
         once, q and out."""
@@ -932,6 +972,9 @@ def main():
         hb = b.hbm_bytes()
         res["hbm"] = {"bytes_per_launch": hb, "GBps": hb / kt / 1e9,
                       "frac": hb / kt / 1e9 / HBM_PEAK_GBS}
+        if not args.no_extras:
+            log("bench: fp8 pool")
+            res["fp8_pool"] = b.fp8_series()
     else:
         kv_bytes = work                   # per launch (one layer)
         step_s = wall / args.steps

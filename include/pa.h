@@ -274,7 +274,11 @@ pa_status pa_decode_multi(void* out, int32_t out_dtype, const void* q, int32_t q
  * The chunk's own K/V must already be in the pool.
  *   q, out            device, packed [total_q][num_heads][head_dim]; sequence
  *                     i owns rows query_start_loc[i] .. query_start_loc[i+1]-1.
- *                     q_dtype = kv_dtype in {f16, bf16}; out_dtype f32 or q_dtype.
+ *                     q_dtype = kv_dtype for f16 and bf16 pools; f16 or bf16
+ *                     for fp8 pools (codes times the pool's per-(block, head)
+ *                     scales, as in pa_decode; |v| * 2^8 must stay within the
+ *                     fp16 range, |v| <= 255 * 448 * scale).  out_dtype f32 or
+ *                     q_dtype.
  *   query_start_loc   device, [num_seqs + 1] int32, non-decreasing, from 0.
  *   context_lens      device, [num_seqs] int32, L_i >= S_i (chunk included).
  *   max_query_len     host bound on every S_i (sizes the grid).

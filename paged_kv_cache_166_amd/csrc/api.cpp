@@ -495,10 +495,14 @@ pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t 
   if (!aligned(q, 16) || !aligned(out, 16))
     return fail(PA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
   if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq <= 0", fn);
-  if (pool->kv_dtype != PA_F16 && pool->kv_dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "%s: kv_dtype %d (built: f16, bf16)", fn, pool->kv_dtype);
-  if (q_dtype != pool->kv_dtype)
+  if (pool->kv_dtype == PA_FP8_E4M3) {
+    if (q_dtype != PA_F16 && q_dtype != PA_BF16)
+      return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype %d (fp8 pools: f16 or bf16)", fn, q_dtype);
+  } else if (pool->kv_dtype != PA_F16 && pool->kv_dtype != PA_BF16) {
+    return fail(PA_ERR_UNSUPPORTED, "%s: kv_dtype %d (built: f16, bf16, fp8)", fn, pool->kv_dtype);
+  } else if (q_dtype != pool->kv_dtype) {
     return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype must equal kv_dtype", fn);
+  }
   if (out_dtype != PA_F32 && out_dtype != q_dtype)
     return fail(PA_ERR_INVALID, "%s: out_dtype must be f32 or q_dtype", fn);
   pa::PrefillArgs a{};
@@ -506,6 +510,8 @@ pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t 
   a.q = q;
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
@@ -514,8 +520,8 @@ pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t 
   a.num_seqs = num_seqs;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_dtype = out_dtype;
-  return hip_status(fn, pa::launch_prefill(a, pool->kv_dtype, pool->head_dim, pool->block_size,
-                                           max_query_len, stream));
+  return hip_status(fn, pa::launch_prefill(a, pool->kv_dtype, q_dtype, pool->head_dim,
+                                           pool->block_size, max_query_len, stream));
 }
 
 }  // extern "C"

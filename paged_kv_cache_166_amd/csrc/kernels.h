@@ -107,6 +107,8 @@ struct PrefillArgs {
   const void* q;
   const void* k_cache;
   const void* v_cache;
+  const float* k_scale;  // fp8 pools: [num_blocks][num_heads]
+  const float* v_scale;
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* query_start_loc;
@@ -126,8 +128,8 @@ struct PrefillArgs {
   int32_t chunk_keys;
 };
 
-hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int block_size,
-                          int max_query_len, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim,
+                          int block_size, int max_query_len, hipStream_t stream);
 hipError_t launch_prefix_partials(const PrefillArgs& a, int kv_dtype, int head_dim,
                                   int block_size, hipStream_t stream);
 

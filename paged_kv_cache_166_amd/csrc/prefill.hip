@@ -183,17 +183,38 @@ __device__ __forceinline__ void load_lds16(const void* src, char* dst) {
 // chunk of the shared prefix (sequence 0's table), no causal mask, and the
 // workgroup writes (max, sum, unnormalised output) per row to the decode
 // workspace instead of the normalised output.
-template <int KV, int D, int BS, bool kPrefix = false>
+// QT: the 16-bit type of q and of the Q K^T MFMAs (the pool's type for
+// 16-bit pools; f16 or bf16 for fp8 pools).  fp8 pools: the E4M3 codes of a
+// tile land in LDS raw, by DMA, and each wave converts the codes its DMA
+// brought to 16 bits (exactly: every E4M3 value is a bf16 and an fp16 value)
+// into the same swizzled row layout the 16-bit pools' DMA produces; the
+// per-(block, head) scales are applied to the scores (K) and to the weights
+// before the P V product (V), so the only added rounding is that of the
+// scaled weights to fp16.
+template <int KV, int QT, int D, int BS, bool kPrefix = false>
 __global__ __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(KV == PA_F16 && D == 128 && BS == 4 ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(KV == PA_FP8_E4M3 || (KV == PA_F16 && D == 128 && BS == 4)
+                                       ? 2 : 3)))
 void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
+  constexpr bool kFp8 = KV == PA_FP8_E4M3;
   constexpr int kRowBytes = D * 2;
   constexpr int kChunks = D / 8;                       // 16-byte chunks per row
   constexpr int kTileBytes = kBN * kRowBytes;
   constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB wave-loads per wave
   constexpr int kRowsPerLoad = 1024 / kRowBytes;
   constexpr int kBlocksPerLoad = kRowsPerLoad > BS ? kRowsPerLoad / BS : 1;
-  constexpr int kOpsPerTile = 2 * kLoadsPerWave;       // vector-memory ops per tile (K + V)
+  // fp8 pools: raw tiles of kBN rows of D bytes, kRawLoads wave-loads each
+  // for K and for V; wave w issues loads w, w + 4, ... of the 2 kRawLoads
+  // (K first), so every wave issues kRawLoadsPerWave per tile.
+  constexpr int kRawTileBytes = kBN * D;
+  constexpr int kRawLoads = kRawTileBytes / 1024;
+  constexpr int kRawLoadsPerWave = 2 * kRawLoads / kWaves;
+  constexpr int kRawRowsPerLoad = 1024 / D;
+  constexpr int kRawPieces = D / 16;                   // 16-byte pieces per raw row
+  constexpr int kRawBlocksPerLoad = kRawRowsPerLoad > BS ? kRawRowsPerLoad / BS : 1;
+  static_assert(!kFp8 || (kRawLoadsPerWave >= 1 && kRawBlocksPerLoad <= 4), "fp8 tile geometry");
+  // vector-memory ops per tile (K + V)
+  constexpr int kOpsPerTile = kFp8 ? kRawLoadsPerWave : 2 * kLoadsPerWave;
   constexpr int kKSteps = D / 16;
   constexpr int kDBlocks = D / 32;
   constexpr int kP = kPrefetch;                        // tiles in flight ahead
@@ -225,6 +246,15 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   };
   auto swz_k = [](int r) { return (r * kChunks / 16) % kChunks; };
   auto swz_v = [](int r) { return 4 * ((r * kChunks / 16) % (kChunks / 4)); };
+  // fp8 pools: raw stages [K codes | V codes] of each tile, linear rows.
+  constexpr int kRawStageBytes = kFp8 ? 2 * kRawTileBytes : 16;
+  __shared__ __attribute__((aligned(1024))) char lds_r0[kRawStageBytes], lds_r1[kRawStageBytes],
+      lds_r2[kRawStageBytes];
+  auto stage_r = [&](auto st) -> char* {
+    if constexpr (decltype(st)::value == 0) return lds_r0;
+    else if constexpr (decltype(st)::value == 1) return lds_r1;
+    else return lds_r2;
+  };
 
   // Work item: (pair = seq * H + head, query tile); pairs are dealt to XCDs
   // round robin by pair, the query tiles of a pair go to the same XCD, last
@@ -281,6 +311,17 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   const_i32* table = (const_i32*)(a.block_tables + int64_t(seq) * a.max_blocks_per_seq);
   const int last_idx = (L - 1) / BS;
   const int64_t last_blk = table[last_idx];
+  // fp8 pools: scales through the constant address space (scalar reads);
+  // register v of a lane holds key 8 (v / 4) + 4 half + v % 4 of a tile, in
+  // its block (key / BS) of the tile's kScaleBlocks.
+  typedef const __attribute__((address_space(4))) float const_f32;
+  const_f32* kscale_c = (const_f32*)a.k_scale;
+  const_f32* vscale_c = (const_f32*)a.v_scale;
+  constexpr int kScaleBlocks = BS >= kBN ? 1 : kBN / BS;
+  auto scale_of = [&](const float (&sc)[kScaleBlocks], int v) {
+    const int k0 = 8 * (v / 4) + (v % 4);
+    return half ? sc[BS >= kBN ? 0 : (k0 + 4) / BS] : sc[BS >= kBN ? 0 : k0 / BS];
+  };
   const int64_t head_off = int64_t(head) * BS * D;      // elements
   const int64_t blk_stride = int64_t(H) * BS * D;
   const uint16_t* kpool = (const uint16_t*)a.k_cache;
@@ -302,9 +343,50 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   const char* kbase0 = (const char*)a.k_cache + int64_t(head) * BS * D * 2;
   const char* vbase0 = (const char*)a.v_cache + int64_t(head) * BS * D * 2;
 
-  // DMA of tile t into K stage dk and V stage dv.
-  auto dma_tile = [&](int t, char* dk, char* dv) {
+  // fp8 pools: this wave's raw wave-loads (K or V, which wave-load of the
+  // tile, the lane's row and 16-byte piece).
+  bool raw_v[kRawLoadsPerWave];
+  int raw_li[kRawLoadsPerWave], raw_row[kRawLoadsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRawLoadsPerWave; ++j) {
+    const int l = wave + kWaves * j;
+    raw_v[j] = l >= kRawLoads;
+    raw_li[j] = l % kRawLoads;
+    raw_row[j] = raw_li[j] * kRawRowsPerLoad + lane / kRawPieces;
+  }
+  const int raw_piece = lane % kRawPieces;
+
+  // DMA of tile t: into K stage dk and V stage dv (16-bit pools), or raw
+  // into dr (fp8 pools).
+  auto dma_tile = [&](int t, char* dk, char* dv, char* dr) {
     const int kb = (t0 + t) * kBN;
+    if constexpr (kFp8) {
+      // Per-lane addresses over at most kRawBlocksPerLoad blocks (scalar
+      // table reads); keys past the end re-read the last key (finite data;
+      // those keys are masked).
+#pragma unroll
+      for (int j = 0; j < kRawLoadsPerWave; ++j) {
+        const int row0 = raw_li[j] * kRawRowsPerLoad;
+        const int b0 = __builtin_amdgcn_readfirstlane((kb + row0) / BS);
+        int64_t blks[kRawBlocksPerLoad];
+#pragma unroll
+        for (int b = 0; b < kRawBlocksPerLoad; ++b)
+          blks[b] = table[__builtin_amdgcn_readfirstlane(min(b0 + b, last_idx))];
+        const int key = kb + raw_row[j];
+        const bool in = key < L;
+        const int keyc = in ? key : L - 1;
+        int64_t blk = last_blk;
+        if (in) {
+#pragma unroll
+          for (int b = 0; b < kRawBlocksPerLoad; ++b)
+            if (key / BS == b0 + b) blk = blks[b];
+        }
+        const int64_t e = (blk * blk_stride + head_off + int64_t(keyc % BS) * D) + raw_piece * 16;
+        const char* src = (const char*)(raw_v[j] ? a.v_cache : a.k_cache) + e;
+        load_lds16(src, dr + (raw_v[j] ? kRawTileBytes : 0) + raw_li[j] * 1024);
+      }
+      return;
+    }
     if (kBlocksPerLoad == 1 && kb + kBN <= L) {
       // Whole tile inside the sequence: one block per wave-load, uniform base.
       const int64_t in_blk = BS > kBN ? int64_t(kb % BS) * kRowBytes : 0;
@@ -345,6 +427,46 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // wave's DMA of that tile has landed, before the barrier that publishes it.
   // (Inline assembly for the same reason as the transposing reads: the
   // compiler would drain the next tile's DMA before reading this stage.)
+  // fp8 pools: the raw pieces this wave's DMA brought into stage st, 16
+  // codes per lane, to 16 bits (K: QT, V: fp16) in the converted stage's
+  // swizzled rows (two 16-byte chunks, 2 piece and 2 piece + 1, per lane).
+  auto own_fp8_convert = [&](auto st) {
+    if constexpr (kFp8) {
+      const char* dr = stage_r(st);
+#pragma unroll
+      for (int j = 0; j < kRawLoadsPerWave; ++j) {
+        const uint32_t ra = uint32_t(reinterpret_cast<uintptr_t>(
+                                (const __attribute__((address_space(3))) char*)dr)) +
+                            (raw_v[j] ? kRawTileBytes : 0) + raw_li[j] * 1024 + lane * 16;
+        u32x4_t w[1];
+        lds_read_b128_x<1>(ra, w);
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float2_t lo = fp8x2_lo(w[0][i]), hi = fp8x2_hi(w[0][i]);
+          if (QT == PA_BF16 && !raw_v[j]) {
+            // every E4M3 value is exact in bf16: its float32 bits, truncated
+            h[2 * i] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+            h[2 * i + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+          } else {
+            h[2 * i] = pack_f16(lo[0], lo[1]);
+            h[2 * i + 1] = pack_f16(hi[0], hi[1]);
+          }
+        }
+        const int row = raw_row[j];
+        char* dst = raw_v[j] ? stage_v(st) : stage_k(st);
+        const int sw = raw_v[j] ? swz_v(row) : swz_k(row);
+        const uint32_t da = uint32_t(reinterpret_cast<uintptr_t>(
+                                (__attribute__((address_space(3))) char*)dst)) + row * kRowBytes;
+        const u32x4_t c0 = {h[0], h[1], h[2], h[3]}, c1 = {h[4], h[5], h[6], h[7]};
+        const uint32_t a0 = da + ((2 * raw_piece) ^ sw) * 16;
+        const uint32_t a1 = da + ((2 * raw_piece + 1) ^ sw) * 16;
+        asm volatile("ds_write_b128 %0, %1" : : "v"(a0), "v"(c0) : "memory");
+        asm volatile("ds_write_b128 %0, %1" : : "v"(a1), "v"(c1) : "memory");
+      }
+    }
+  };
+
   auto own_v_to_f16 = [&](char* dv) {
     if constexpr (KV == PA_BF16) {
       const uint32_t a0 =
@@ -387,10 +509,11 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  dma_tile(0, stage_k(S0{}), stage_v(S0{}));
-  dma_tile(min(1, n_tiles - 1), stage_k(S1{}), stage_v(S1{}));
+  dma_tile(0, stage_k(S0{}), stage_v(S0{}), stage_r(S0{}));
+  dma_tile(min(1, n_tiles - 1), stage_k(S1{}), stage_v(S1{}), stage_r(S1{}));
   __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile 0 landed
   own_v_to_f16(stage_v(S0{}));
+  own_fp8_convert(S0{});
   wg_barrier();
 
   // One tile: issue tile t+2 (stage st+2), consume tile t (stage st), wait
@@ -413,17 +536,29 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     // only tile t+1, issued an iteration ago.
     const uint4 kf0 = active ? kfrag(0) : make_uint4(0, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    dma_tile(min(t + 2, n_tiles - 1), stage_k(Snn{}), stage_v(Snn{}));
+    dma_tile(min(t + 2, n_tiles - 1), stage_k(Snn{}), stage_v(Snn{}), stage_r(Snn{}));
     __builtin_amdgcn_sched_barrier(0);
     if (active) {
       const char* vl = stage_v(st);
+      // fp8 pools: the K and V scales of the tile's blocks (scalar reads,
+      // issued before the MFMAs that they wait behind).
+      float sk[kScaleBlocks], sv[kScaleBlocks];
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int j = 0; j < kScaleBlocks; ++j) {
+          const int64_t blk =
+              table[__builtin_amdgcn_readfirstlane(min((kb + j * BS) / BS, last_idx))];
+          sk[j] = kscale_c[blk * H + head];
+          sv[j] = vscale_c[blk * H + head];
+        }
+      }
       // S^T = K Q^T : rows = keys of the tile, columns = this wave's queries.
       f32x16_t s;
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = 0.f;
-      s = mfma_qk<KV>(kf0, qf[0], s);
+      s = mfma_qk<QT>(kf0, qf[0], s);
 #pragma unroll
-      for (int kk = 1; kk < kKSteps; ++kk) s = mfma_qk<KV>(kfrag(kk), qf[kk], s);
+      for (int kk = 1; kk < kKSteps; ++kk) s = mfma_qk<QT>(kfrag(kk), qf[kk], s);
       // Register v of this lane holds key 8*(v/4) + 4*half + v%4 of the tile.
       // Scores stay unscaled here; c = scale*log2(e) > 0 is folded into the
       // exponent below.
@@ -433,7 +568,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       const float c = a.scale_log2;
       float x[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) x[v] = s[v];
+      for (int v = 0; v < 16; ++v) x[v] = kFp8 ? s[v] * scale_of(sk, v) : s[v];
       if (kb + kBN - 1 > tile_lim) {  // the tile crosses the causal diagonal (or the chunk end)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -476,6 +611,11 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       // P^T as B operands: k-step tt takes accumulator registers 8tt .. 8tt+7,
       // i.e. keys 16tt + 8*(e/4) + 4*half + e%4 for e = 0..7.
       uint4 pf[2];
+      if constexpr (kFp8) {
+        // the V scales go with the weights (the row sum above is unscaled)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] *= scale_of(sv, v);
+      }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         pf[tt] = make_uint4(pack_f16(x[8 * tt + 0], x[8 * tt + 1]),
@@ -507,7 +647,10 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       pv_step(std::integral_constant<int, 1>{});
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile t+1 landed
-    if (t + 1 < n_tiles) own_v_to_f16(stage_v(Sn{}));
+    if (t + 1 < n_tiles) {
+      own_v_to_f16(stage_v(Sn{}));
+      own_fp8_convert(Sn{});
+    }
     wg_barrier();
   };
   // The first iteration is peeled so that both edges into the loop come
@@ -556,26 +699,26 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   }
 }
 
-template <int KV, int D, int BS>
+template <int KV, int QT, int D, int BS>
 hipError_t launch_t(const PrefillArgs& a, int max_query_len, hipStream_t stream) {
   const int num_qtiles = (max_query_len + kBM - 1) / kBM;
   const int num_pairs = a.num_seqs * a.num_heads;
   const int padded_pairs = (num_pairs + kXcds - 1) / kXcds * kXcds;
   const int64_t blocks = int64_t(padded_pairs) * num_qtiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<KV, D, BS>), dim3(unsigned(blocks)), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((prefill_kernel<KV, QT, D, BS>), dim3(unsigned(blocks)), dim3(kWaves * 64), 0,
                      stream, a, num_qtiles, num_pairs);
   return hipGetLastError();
 }
 
-template <int KV, int D>
+template <int KV, int QT, int D>
 hipError_t launch_bs(const PrefillArgs& a, int bs, int mq, hipStream_t stream) {
   switch (bs) {
-    case 4: return launch_t<KV, D, 4>(a, mq, stream);
-    case 8: return launch_t<KV, D, 8>(a, mq, stream);
-    case 16: return launch_t<KV, D, 16>(a, mq, stream);
-    case 32: return launch_t<KV, D, 32>(a, mq, stream);
-    case 64: return launch_t<KV, D, 64>(a, mq, stream);
+    case 4: return launch_t<KV, QT, D, 4>(a, mq, stream);
+    case 8: return launch_t<KV, QT, D, 8>(a, mq, stream);
+    case 16: return launch_t<KV, QT, D, 16>(a, mq, stream);
+    case 32: return launch_t<KV, QT, D, 32>(a, mq, stream);
+    case 64: return launch_t<KV, QT, D, 64>(a, mq, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -588,8 +731,8 @@ hipError_t launch_prefix_t(const PrefillArgs& a, hipStream_t stream) {
   const int padded_pairs = (num_pairs + kXcds - 1) / kXcds * kXcds;
   const int64_t blocks = int64_t(padded_pairs) * num_qtiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<KV, D, BS, true>), dim3(unsigned(blocks)), dim3(kWaves * 64),
-                     0, stream, a, num_qtiles, num_pairs);
+  hipLaunchKernelGGL((prefill_kernel<KV, KV, D, BS, true>), dim3(unsigned(blocks)),
+                     dim3(kWaves * 64), 0, stream, a, num_qtiles, num_pairs);
   return hipGetLastError();
 }
 
@@ -612,19 +755,24 @@ hipError_t launch_prefix_d(const PrefillArgs& a, int d, int bs, hipStream_t stre
   return hipErrorInvalidValue;
 }
 
-template <int KV>
+template <int KV, int QT>
 hipError_t launch_d(const PrefillArgs& a, int d, int bs, int mq, hipStream_t stream) {
-  if (d == 64) return launch_bs<KV, 64>(a, bs, mq, stream);
-  if (d == 128) return launch_bs<KV, 128>(a, bs, mq, stream);
+  if (d == 64) return launch_bs<KV, QT, 64>(a, bs, mq, stream);
+  if (d == 128) return launch_bs<KV, QT, 128>(a, bs, mq, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int block_size,
-                          int max_query_len, hipStream_t stream) {
-  if (kv_dtype == PA_BF16) return launch_d<PA_BF16>(a, head_dim, block_size, max_query_len, stream);
-  if (kv_dtype == PA_F16) return launch_d<PA_F16>(a, head_dim, block_size, max_query_len, stream);
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim,
+                          int block_size, int max_query_len, hipStream_t stream) {
+  const int mq = max_query_len;
+  if (kv_dtype == PA_BF16) return launch_d<PA_BF16, PA_BF16>(a, head_dim, block_size, mq, stream);
+  if (kv_dtype == PA_F16) return launch_d<PA_F16, PA_F16>(a, head_dim, block_size, mq, stream);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16)
+    return launch_d<PA_FP8_E4M3, PA_BF16>(a, head_dim, block_size, mq, stream);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16)
+    return launch_d<PA_FP8_E4M3, PA_F16>(a, head_dim, block_size, mq, stream);
   return hipErrorInvalidValue;
 }
 

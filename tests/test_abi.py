@@ -106,6 +106,11 @@ def test_reshape_and_prefill_checks():
                                 ctypes.byref(f32), ctypes.c_void_p(0x3000), 4, ctypes.c_void_p(0x4000),
                                 ctypes.c_void_p(0x5000), 1, 16, 0.1, None)
     assert r == pa.PA_ERR_UNSUPPORTED
+    fp8 = _fake_pool(kv_dtype=pa.PA_FP8_E4M3, k_scale=0x70000, v_scale=0x80000)
+    r = pa.lib.pa_prefill_chunk(ctypes.c_void_p(0x1000), pa.PA_F32, ctypes.c_void_p(0x2000), pa.PA_F32,
+                                ctypes.byref(fp8), ctypes.c_void_p(0x3000), 4, ctypes.c_void_p(0x4000),
+                                ctypes.c_void_p(0x5000), 1, 16, 0.1, None)
+    assert r == pa.PA_ERR_UNSUPPORTED                                   # fp8 pool, f32 queries
     r = pa.lib.pa_copy_blocks(ctypes.byref(p), None, 3, None)
     assert r == pa.PA_ERR_INVALID
 

@@ -117,3 +117,48 @@ def test_prefill_empty_chunks_and_no_op_calls():
     pa.pa_prefill_chunk(out, q_dev, sc.pool, t_dev, ln_dev, qsl_dev, 0, scale)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("qdt", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [4, 8, 16, 32, 64])
+def test_prefill_fp8_pool(qdt, D, bs):
+    """fp8 E4M3 pools (per-(block, head) scales) with bf16 or fp16 queries:
+    contexts 0 .. 700, chunks of 1 .. 200 rows, against the oracle fed the
+    same codes and scales (tolerance 2e-2; the codes are exact in 16 bits,
+    only the scaled weights are rounded)."""
+    ctx = [0, 5, 37, 700, 130]
+    chunk = [17, 1, 128, 200, 129]
+    N = sum(-(-(c + s) // bs) for c, s in zip(ctx, chunk)) + 5
+    sc = Scenario(N, 2, bs, D, "fp8", seed=51 + bs + D, in_dtype=qdt, scale_range=(0.011, 0.03))
+    seqs, qsl, q_dev, q64 = _setup(sc, ctx, chunk, qdt)
+    scale = 1 / math.sqrt(D)
+    tables, lens = sc.oracle_tables(seqs)
+    ref = A.prefill_chunk(q64, qsl, sc.ok, sc.ov, "fp8", tables, lens, bs, scale,
+                          k_scale=sc.oks, v_scale=sc.ovs)
+    got = _run(sc, seqs, qsl, q_dev, scale)
+    err = assert_close(got, ref, TOL["fp8"], f"fp8 prefill q={qdt} D={D} bs={bs}")
+    rel = err / np.max(np.abs(ref))
+    assert rel < 5e-3, f"relative error {rel:.2e}"
+    got = _run(sc, seqs, qsl, q_dev, scale, out_dtype=pa.TORCH_DTYPE[qdt])
+    assert np.all(np.abs(got - ref) <= TOL["fp8"] + half_ulp(qdt, ref)), "low-precision output"
+
+
+def test_prefill_fp8_chunked_workload_shape():
+    """The chunked-prefill shape (512-row chunks, 32 heads x 128, block 32)
+    over an fp8 pool with bf16 queries, contexts up to 2500: three heads of
+    every sequence against the oracle."""
+    ctx = [2500, 0, 977, 31]
+    chunk = [512, 512, 300, 512]
+    bs, H, D = 32, 32, 128
+    N = sum(-(-(c + s) // bs) for c, s in zip(ctx, chunk)) + 3
+    sc = Scenario(N, H, bs, D, "fp8", seed=57, in_dtype="bf16", scale_range=(0.011, 0.03))
+    seqs, qsl, q_dev, q64 = _setup(sc, ctx, chunk, "bf16")
+    scale = 1 / math.sqrt(D)
+    got = _run(sc, seqs, qsl, q_dev, scale)
+    tables, lens = sc.oracle_tables(seqs)
+    heads = [0, 17, 31]
+    ref = A.prefill_chunk(q64, qsl, sc.ok, sc.ov, "fp8", tables, lens, bs, scale, heads=heads,
+                          k_scale=sc.oks, v_scale=sc.ovs)
+    err = assert_close(got[:, heads], ref[:, heads], TOL["fp8"], "fp8 chunked prefill")
+    print(f"fp8 chunked prefill: max abs err {err:.2e}")
