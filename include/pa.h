@@ -221,8 +221,9 @@ pa_status pa_decode_append(void* out, int32_t out_dtype, const void* q, int32_t 
  *                 context covers them (context_lens[i] >= shared_blocks *
  *                 block_size); 1 <= shared_blocks <= max_blocks_per_seq.  Not
  *                 checked on the device.
- * f16 and bf16 pools only (PA_ERR_UNSUPPORTED otherwise); q of the pool's
- * type.  A workspace is always needed:
+ * f16, bf16 and fp8 pools (PA_ERR_UNSUPPORTED for f32); q of the pool's
+ * type, or f16 / bf16 for fp8 pools (the prefix pass runs on MFMA).  A
+ * workspace is always needed:
  * pa_decode_shared_prefix_workspace_bytes(...).  Other arguments as pa_decode.
  */
 size_t pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_seqs,

@@ -313,17 +313,21 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
                                   size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "pa_decode_shared_prefix";
   if (pa_status st = check_pool(fn, pool)) return st;
-  if (pool->kv_dtype != PA_F16 && pool->kv_dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "%s: f16 or bf16 pools (the prefix pass runs on MFMA)", fn);
+
   if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "%s: num_seqs %d", fn, num_seqs);
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
   if (!aligned(q, 16) || !aligned(out, 16))
     return fail(PA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
-  if (q_dtype != pool->kv_dtype)
-    return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype %d must equal kv_dtype %d", fn, q_dtype,
+  // the prefix pass runs on MFMA: 16-bit queries (the pool's type, or f16 /
+  // bf16 for fp8 pools)
+  if (pool->kv_dtype == PA_FP8_E4M3 ? (q_dtype != PA_F16 && q_dtype != PA_BF16)
+                                    : q_dtype != pool->kv_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype %d with kv_dtype %d", fn, q_dtype,
                 pool->kv_dtype);
+  if (pool->kv_dtype == PA_F32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: f32 pools (the prefix pass runs on MFMA)", fn);
   if (out_dtype != PA_F32 && out_dtype != q_dtype)
     return fail(PA_ERR_INVALID, "%s: out_dtype must be f32 or q_dtype", fn);
   if (shared_blocks <= 0 || shared_blocks > max_blocks_per_seq)
@@ -351,6 +355,8 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
   pf.q = q;
   pf.k_cache = pool->k_cache;
   pf.v_cache = pool->v_cache;
+  pf.k_scale = pool->k_scale;
+  pf.v_scale = pool->v_scale;
   pf.block_tables = block_tables;  // sequence 0's row holds the prefix
   pf.max_blocks_per_seq = max_blocks_per_seq;
   pf.num_heads = pool->num_heads;
@@ -362,7 +368,7 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
   pf.max_parts = w.parts;
   pf.prefix_len = g.prefix_len;
   pf.chunk_keys = g.chunk_keys;
-  if (pa_status st = hip_status(fn, pa::launch_prefix_partials(pf, pool->kv_dtype, pool->head_dim,
+  if (pa_status st = hip_status(fn, pa::launch_prefix_partials(pf, pool->kv_dtype, q_dtype, pool->head_dim,
                                                                pool->block_size, stream)))
     return st;
 

@@ -130,7 +130,7 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim,
                           int block_size, int max_query_len, hipStream_t stream);
-hipError_t launch_prefix_partials(const PrefillArgs& a, int kv_dtype, int head_dim,
+hipError_t launch_prefix_partials(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim,
                                   int block_size, hipStream_t stream);
 
 }  // namespace pa

@@ -723,7 +723,7 @@ hipError_t launch_bs(const PrefillArgs& a, int bs, int mq, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-template <int KV, int D, int BS>
+template <int KV, int QT, int D, int BS>
 hipError_t launch_prefix_t(const PrefillArgs& a, hipStream_t stream) {
   const int num_qtiles = (a.num_seqs + kBM - 1) / kBM;
   const int chunks = (a.prefix_len + a.chunk_keys - 1) / a.chunk_keys;
@@ -731,27 +731,27 @@ hipError_t launch_prefix_t(const PrefillArgs& a, hipStream_t stream) {
   const int padded_pairs = (num_pairs + kXcds - 1) / kXcds * kXcds;
   const int64_t blocks = int64_t(padded_pairs) * num_qtiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<KV, KV, D, BS, true>), dim3(unsigned(blocks)),
+  hipLaunchKernelGGL((prefill_kernel<KV, QT, D, BS, true>), dim3(unsigned(blocks)),
                      dim3(kWaves * 64), 0, stream, a, num_qtiles, num_pairs);
   return hipGetLastError();
 }
 
-template <int KV, int D>
+template <int KV, int QT, int D>
 hipError_t launch_prefix_bs(const PrefillArgs& a, int bs, hipStream_t stream) {
   switch (bs) {
-    case 4: return launch_prefix_t<KV, D, 4>(a, stream);
-    case 8: return launch_prefix_t<KV, D, 8>(a, stream);
-    case 16: return launch_prefix_t<KV, D, 16>(a, stream);
-    case 32: return launch_prefix_t<KV, D, 32>(a, stream);
-    case 64: return launch_prefix_t<KV, D, 64>(a, stream);
+    case 4: return launch_prefix_t<KV, QT, D, 4>(a, stream);
+    case 8: return launch_prefix_t<KV, QT, D, 8>(a, stream);
+    case 16: return launch_prefix_t<KV, QT, D, 16>(a, stream);
+    case 32: return launch_prefix_t<KV, QT, D, 32>(a, stream);
+    case 64: return launch_prefix_t<KV, QT, D, 64>(a, stream);
   }
   return hipErrorInvalidValue;
 }
 
-template <int KV>
+template <int KV, int QT>
 hipError_t launch_prefix_d(const PrefillArgs& a, int d, int bs, hipStream_t stream) {
-  if (d == 64) return launch_prefix_bs<KV, 64>(a, bs, stream);
-  if (d == 128) return launch_prefix_bs<KV, 128>(a, bs, stream);
+  if (d == 64) return launch_prefix_bs<KV, QT, 64>(a, bs, stream);
+  if (d == 128) return launch_prefix_bs<KV, QT, 128>(a, bs, stream);
   return hipErrorInvalidValue;
 }
 
@@ -776,10 +776,14 @@ hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int q_dtype, int h
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefix_partials(const PrefillArgs& a, int kv_dtype, int head_dim,
+hipError_t launch_prefix_partials(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim,
                                   int block_size, hipStream_t stream) {
-  if (kv_dtype == PA_BF16) return launch_prefix_d<PA_BF16>(a, head_dim, block_size, stream);
-  if (kv_dtype == PA_F16) return launch_prefix_d<PA_F16>(a, head_dim, block_size, stream);
+  if (kv_dtype == PA_BF16) return launch_prefix_d<PA_BF16, PA_BF16>(a, head_dim, block_size, stream);
+  if (kv_dtype == PA_F16) return launch_prefix_d<PA_F16, PA_F16>(a, head_dim, block_size, stream);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16)
+    return launch_prefix_d<PA_FP8_E4M3, PA_BF16>(a, head_dim, block_size, stream);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16)
+    return launch_prefix_d<PA_FP8_E4M3, PA_F16>(a, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }
 

@@ -18,10 +18,10 @@ from tests.test_gpu_decode import _oracle
 pytestmark = pytest.mark.gpu
 
 
-def _batch(kv, D, bs, H, shared_blocks, own, seed):
+def _batch(kv, D, bs, H, shared_blocks, own, seed, **kw):
     """Sequence 0 holds the prefix; the others fork it; then own tokens."""
     N = shared_blocks + sum(-(-n // bs) for n in own) + len(own) + 4
-    sc = Scenario(N, H, bs, D, kv, seed=seed)
+    sc = Scenario(N, H, bs, D, kv, seed=seed, **kw)
     sc.prompt(0, shared_blocks * bs)
     for i in range(1, len(own)):
         sc.fork(0, i)
@@ -101,8 +101,13 @@ def test_refusals():
     q = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
     out = torch.empty((1, 2, 128), dtype=torch.float32, device="cuda")
     ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
-    with pytest.raises(NotImplementedError):
-        pa.pa_decode_shared_prefix(out, q, sc.pool, t_dev, ln_dev, 1, 0.1, 0, ws)
+    with pytest.raises(NotImplementedError):                   # fp8 pool, f32 queries
+        pa.pa_decode_shared_prefix(out, q.float(), sc.pool, t_dev, ln_dev, 1, 0.1, 0, ws)
+    sc3 = Scenario(8, 2, 16, 128, "f32", seed=3)
+    sc3.prompt(0, 32)
+    t3, l3, _, _ = sc3.device_tables([0])
+    with pytest.raises(NotImplementedError):                   # f32 pool
+        pa.pa_decode_shared_prefix(out, q.float(), sc3.pool, t3, l3, 1, 0.1, 0, ws)
     sc2 = Scenario(8, 2, 16, 128, "bf16", seed=3)
     sc2.prompt(0, 32)
     t2, l2, _, _ = sc2.device_tables([0])
@@ -110,3 +115,29 @@ def test_refusals():
         pa.pa_decode_shared_prefix(out, q, sc2.pool, t2, l2, 0, 0.1, 0, ws)   # no shared block
     with pytest.raises(ValueError):
         pa.pa_decode_shared_prefix(out, q, sc2.pool, t2, l2, 1, 0.1, 0, ws[:16])  # workspace
+
+
+@pytest.mark.parametrize("qdt", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_fp8_pool(qdt, D, bs):
+    """fp8 E4M3 pools with f16 or bf16 queries: the prefix pass over the
+    codes and their scales, against the oracle (tolerance 2e-2) and against
+    pa_decode of the same batch."""
+    H = 3
+    for shared_blocks, own in [(1, [0, 1, 5, 40]), (max(1, 600 // bs), [3, 0, 77, 200, 1])]:
+        sc = _batch("fp8", D, bs, H, shared_blocks, own, seed=bs + D + shared_blocks,
+                    in_dtype=qdt, scale_range=(0.011, 0.03))
+        seqs = list(range(len(own)))
+        q_dev, q64 = sc.random_q(len(seqs), qdt)
+        scale = 1 / math.sqrt(D)
+        ref = _oracle(sc, seqs, q64, scale)
+        got = _run(sc, seqs, q_dev, shared_blocks, scale)
+        err = assert_close(got, ref, TOL["fp8"], f"fp8 q={qdt} D={D} bs={bs} prefix={shared_blocks}")
+        assert err / np.max(np.abs(ref)) < 5e-3
+        t_dev, ln_dev, _, _ = sc.device_tables(seqs)
+        plain = torch.empty(q_dev.shape, dtype=torch.float32, device="cuda")
+        pa.pa_decode(plain, q_dev, sc.pool, t_dev, ln_dev, scale, 0,
+                     pa.decode_workspace(sc.pool, len(seqs), t_dev.shape[1]))
+        torch.cuda.synchronize()
+        assert np.max(np.abs(got - plain.cpu().numpy())) < 1e-3
