@@ -281,7 +281,9 @@ pa_status pa_decode_multi(void* out, int32_t out_dtype, const void* q, int32_t q
  *                     fp16 range, |v| <= 255 * 448 * scale).  out_dtype f32 or
  *                     q_dtype.
  *   query_start_loc   device, [num_seqs + 1] int32, non-decreasing, from 0.
- *   context_lens      device, [num_seqs] int32, L_i >= S_i (chunk included).
+ *   context_lens      device, [num_seqs] int32, S_i <= L_i <=
+ *                     max_blocks_per_seq * block_size (chunk included); the
+ *                     first ceil(L_i / block_size) table entries are read.
  *   max_query_len     host bound on every S_i (sizes the grid).
  */
 pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
