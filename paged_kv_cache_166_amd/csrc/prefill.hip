@@ -356,9 +356,20 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   }
   const int raw_piece = lane % kRawPieces;
 
+  // The wave-loads of one wave cover kWaveRows consecutive rows of a tile.
+  // When a block holds at least that many, they all fall in one block: the
+  // wave reads one table entry per tile, and reads it an iteration ahead
+  // (blk_hint), so that its latency hides behind the tile in between.
+  constexpr int kWaveRows = kLoadsPerWave * kRowsPerLoad;
+  constexpr bool kOneBlockPerWave = !kFp8 && kBlocksPerLoad == 1 && kWaveRows <= BS;
+  auto wave_blk = [&](int t) -> int64_t {
+    return table[__builtin_amdgcn_readfirstlane(
+        min(((t0 + t) * kBN + wave * kWaveRows) / BS, last_idx))];
+  };
+
   // DMA of tile t: into K stage dk and V stage dv (16-bit pools), or raw
-  // into dr (fp8 pools).
-  auto dma_tile = [&](int t, char* dk, char* dv, char* dr) {
+  // into dr (fp8 pools).  blk_hint: wave_blk(t) where kOneBlockPerWave.
+  auto dma_tile = [&](int t, char* dk, char* dv, char* dr, int64_t blk_hint) {
     const int kb = (t0 + t) * kBN;
     if constexpr (kFp8) {
       // Per-lane addresses over at most kRawBlocksPerLoad blocks (scalar
@@ -393,7 +404,9 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int li = wave * kLoadsPerWave + i;
-        const int64_t blk = table[__builtin_amdgcn_readfirstlane((kb + li * kRowsPerLoad) / BS)];
+        const int64_t blk =
+            kOneBlockPerWave ? blk_hint
+                             : table[__builtin_amdgcn_readfirstlane((kb + li * kRowsPerLoad) / BS)];
         load_lds16(kbase0 + blk * tile_stride + in_blk + off_k[i], dk + li * 1024);
         load_lds16(vbase0 + blk * tile_stride + in_blk + off_v[i], dv + li * 1024);
       }
@@ -509,8 +522,12 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  dma_tile(0, stage_k(S0{}), stage_v(S0{}), stage_r(S0{}));
-  dma_tile(min(1, n_tiles - 1), stage_k(S1{}), stage_v(S1{}), stage_r(S1{}));
+  const int t_1 = min(1, n_tiles - 1);
+  dma_tile(0, stage_k(S0{}), stage_v(S0{}), stage_r(S0{}), kOneBlockPerWave ? wave_blk(0) : 0);
+  dma_tile(t_1, stage_k(S1{}), stage_v(S1{}), stage_r(S1{}),
+           kOneBlockPerWave ? wave_blk(t_1) : 0);
+  // the table entry of the tile the next iteration issues
+  int64_t blk_next = kOneBlockPerWave ? wave_blk(min(2, n_tiles - 1)) : 0;
   __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile 0 landed
   own_v_to_f16(stage_v(S0{}));
   own_fp8_convert(S0{});
@@ -536,7 +553,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     // only tile t+1, issued an iteration ago.
     const uint4 kf0 = active ? kfrag(0) : make_uint4(0, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    dma_tile(min(t + 2, n_tiles - 1), stage_k(Snn{}), stage_v(Snn{}), stage_r(Snn{}));
+    dma_tile(min(t + 2, n_tiles - 1), stage_k(Snn{}), stage_v(Snn{}), stage_r(Snn{}), blk_next);
+    if constexpr (kOneBlockPerWave) blk_next = wave_blk(min(t + 3, n_tiles - 1));
     __builtin_amdgcn_sched_barrier(0);
     if (active) {
       const char* vl = stage_v(st);
