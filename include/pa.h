@@ -18,8 +18,10 @@
  *   kernel surface at the caller's next synchronisation of the stream.
  * - Host-side checks: null pointers, dtype combinations, head_dim in {64,128},
  *   block_size in {4,8,16,32,64}, 16-byte alignment of every device pointer,
- *   workspace size.  Block-table entries and slots are trusted: the caller
- *   keeps them in [0, num_blocks) (the allocator below produces only such).
+ *   workspace size, and table rows of 1..INT32_MAX / block_size entries
+ *   (max_blocks_per_seq; lengths are int32, so no row can address more).
+ *   Block-table entries and slots are trusted: the caller keeps them in
+ *   [0, num_blocks) (the allocator below produces only such).
  * - Pool layout: K and V are each [num_blocks][num_heads][block_size][head_dim]
  *   of kv_dtype, so one (block, head) tile is contiguous (block_size*head_dim
  *   elements; 4 KiB for 16 x 128 fp16).  Pool bases must be 128-byte aligned,
@@ -144,9 +146,9 @@ int32_t pa_decode_auto_partition_blocks(const pa_pool* pool, int32_t num_seqs,
 
 /*
  * Bytes of device workspace pa_decode needs for these arguments (0 when every
- * sequence fits in one partition): the (max, sum) pair and the unnormalised
- * output of every (sequence, head, partition), float32.  No initialisation is
- * needed.
+ * sequence fits in one partition, and for arguments pa_decode would refuse):
+ * the (max, sum) pair and the unnormalised output of every (sequence, head,
+ * partition), float32.  No initialisation is needed.
  */
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
                                  int32_t max_blocks_per_seq, int32_t partition_blocks);

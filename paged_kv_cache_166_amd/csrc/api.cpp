@@ -3,6 +3,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 
 #include "kernels.h"
@@ -40,6 +41,12 @@ pa_status check_pool(const char* fn, const pa_pool* p) {
     if (!p->k_scale || !p->v_scale) return fail(PA_ERR_INVALID, "%s: fp8 pool without scales", fn);
   }
   return PA_OK;
+}
+
+// A table row addresses at most INT32_MAX tokens (context lengths are
+// int32); a wider row would overflow the partition arithmetic below.
+bool row_fits(const pa_pool* p, int32_t max_blocks) {
+  return max_blocks > 0 && int64_t(max_blocks) * p->block_size <= INT32_MAX;
 }
 
 pa_status hip_status(const char* fn, hipError_t e) {
@@ -85,7 +92,7 @@ PrefixPlan prefix_plan(const pa_pool* p, int32_t max_blocks, int32_t shared_bloc
                        int32_t partition_blocks) {
   PrefixPlan g{};
   g.prefix_len = shared_blocks * p->block_size;
-  const int32_t want = (g.prefix_len + 63) / 64;
+  const int32_t want = int32_t((int64_t(g.prefix_len) + 63) / 64);
   g.chunk_keys = std::max<int32_t>(128, (want + 31) / 32 * 32);
   g.chunks = (g.prefix_len + g.chunk_keys - 1) / g.chunk_keys;
   g.suffix_pb = partition_blocks > 0 ? partition_blocks : auto_partition_blocks(p);
@@ -116,7 +123,9 @@ pa_status check_multi(const char* fn, const pa_pool* pools, int32_t num_groups,
     if (part_tokens % bs != 0 || part_tokens / bs > 256)
       return fail(PA_ERR_UNSUPPORTED,
                   "%s: partition of %d tokens is not 1..256 blocks of %d", fn, part_tokens, bs);
-    if (max_blocks[g] <= 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq <= 0", fn);
+    if (!row_fits(&pools[g], max_blocks[g]))
+      return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq %d (1..INT32_MAX / block_size)", fn,
+                  max_blocks[g]);
     const int64_t p = (int64_t(max_blocks[g]) * bs + part_tokens - 1) / part_tokens;
     if (p > kMaxParts)
       return fail(PA_ERR_UNSUPPORTED, "%s: %lld partitions per sequence (at most %d)", fn,
@@ -184,7 +193,9 @@ int32_t pa_decode_auto_partition_blocks(const pa_pool* pool, int32_t num_seqs,
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
                                  int32_t max_blocks_per_seq, int32_t partition_blocks) {
   if (check_pool("pa_decode_workspace_bytes", pool)) return 0;
-  if (num_seqs <= 0 || max_blocks_per_seq <= 0) return 0;
+  if (num_seqs <= 0 || !row_fits(pool, max_blocks_per_seq) || partition_blocks < 0 ||
+      partition_blocks > 256)
+    return 0;
   const int32_t pb = partition_blocks > 0 ? partition_blocks : auto_partition_blocks(pool);
   return size_t(ws_layout(pool, num_seqs, max_blocks_per_seq, pb).bytes);
 }
@@ -208,7 +219,9 @@ pa_status decode_impl(const char* fn, void* out, int32_t out_dtype, const void* 
     return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
   if (!aligned(q, 16) || !aligned(out, 16))
     return fail(PA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
-  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq <= 0", fn);
+  if (!row_fits(pool, max_blocks_per_seq))
+    return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq %d (1..INT32_MAX / block_size)", fn,
+                max_blocks_per_seq);
   if (pool->kv_dtype == PA_FP8_E4M3) {
     if (!valid_io_dtype(q_dtype)) return fail(PA_ERR_INVALID, "%s: q_dtype %d", fn, q_dtype);
   } else if (q_dtype != pool->kv_dtype) {
@@ -297,8 +310,8 @@ size_t pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_
                                                int32_t max_blocks_per_seq, int32_t shared_blocks,
                                                int32_t partition_blocks) {
   if (check_pool("pa_decode_shared_prefix_workspace_bytes", pool)) return 0;
-  if (num_seqs <= 0 || shared_blocks <= 0 || shared_blocks > max_blocks_per_seq ||
-      partition_blocks < 0 || partition_blocks > 256)
+  if (num_seqs <= 0 || !row_fits(pool, max_blocks_per_seq) || shared_blocks <= 0 ||
+      shared_blocks > max_blocks_per_seq || partition_blocks < 0 || partition_blocks > 256)
     return 0;
   const PrefixPlan g = prefix_plan(pool, max_blocks_per_seq, shared_blocks, partition_blocks);
   // always a workspace: the prefix's partials are merged even alone
@@ -330,6 +343,9 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
     return fail(PA_ERR_UNSUPPORTED, "%s: f32 pools (the prefix pass runs on MFMA)", fn);
   if (out_dtype != PA_F32 && out_dtype != q_dtype)
     return fail(PA_ERR_INVALID, "%s: out_dtype must be f32 or q_dtype", fn);
+  if (!row_fits(pool, max_blocks_per_seq))
+    return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq %d (1..INT32_MAX / block_size)", fn,
+                max_blocks_per_seq);
   if (shared_blocks <= 0 || shared_blocks > max_blocks_per_seq)
     return fail(PA_ERR_INVALID, "%s: shared_blocks %d (1..max_blocks_per_seq %d)", fn,
                 shared_blocks, max_blocks_per_seq);
@@ -500,7 +516,9 @@ pa_status pa_prefill_chunk(void* out, int32_t out_dtype, const void* q, int32_t 
     return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
   if (!aligned(q, 16) || !aligned(out, 16))
     return fail(PA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
-  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq <= 0", fn);
+  if (!row_fits(pool, max_blocks_per_seq))
+    return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq %d (1..INT32_MAX / block_size)", fn,
+                max_blocks_per_seq);
   if (pool->kv_dtype == PA_FP8_E4M3) {
     if (q_dtype != PA_F16 && q_dtype != PA_BF16)
       return fail(PA_ERR_UNSUPPORTED, "%s: q_dtype %d (fp8 pools: f16 or bf16)", fn, q_dtype);

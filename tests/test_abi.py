@@ -184,3 +184,29 @@ def test_decode_refuses_more_partitions_than_the_grid_holds():
     assert _decode(_fake_pool(), maxb=70000, pb=1) == pa.PA_ERR_UNSUPPORTED
     assert b"partitions" in pa.lib.pa_last_error()
     assert _decode(_fake_pool(), maxb=70000, pb=2) != pa.PA_ERR_UNSUPPORTED   # 35000 partitions
+
+
+def test_table_rows_wider_than_int32_tokens_are_refused():
+    """A table row can address at most INT32_MAX tokens (context lengths are
+    int32): wider rows are refused before any partition arithmetic, and the
+    workspace queries return 0 for every argument the calls would refuse."""
+    p = _fake_pool()                                   # 16-token blocks
+    widest = (2**31 - 1) // 16
+    r = _decode(p, maxb=widest, pb=1)
+    assert r == pa.PA_ERR_UNSUPPORTED                  # accepted row, too many partitions
+    assert b"partitions" in pa.lib.pa_last_error()
+    for maxb in (widest + 1, 2**31 - 1):
+        assert _decode(p, maxb=maxb, pb=256) == pa.PA_ERR_INVALID
+        assert b"max_blocks_per_seq" in pa.lib.pa_last_error()
+        assert pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 4, maxb, 16) == 0
+        assert pa.lib.pa_decode_shared_prefix_workspace_bytes(ctypes.byref(p), 4, maxb, 1, 0) == 0
+        r = pa.lib.pa_prefill_chunk(ctypes.c_void_p(0x1000), pa.PA_F32, ctypes.c_void_p(0x2000),
+                                    pa.PA_F16, ctypes.byref(p), ctypes.c_void_p(0x3000), maxb,
+                                    ctypes.c_void_p(0x4000), ctypes.c_void_p(0x5000), 1, 16, 0.1,
+                                    None)
+        assert r == pa.PA_ERR_INVALID
+    assert pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 4, widest, 0) > 0
+    # partition sizes pa_decode refuses give no workspace size either
+    for pb in (-1, 257):
+        assert pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 4, 33, pb) == 0
+        assert _decode(p, maxb=33, pb=pb) == pa.PA_ERR_UNSUPPORTED
