@@ -322,7 +322,9 @@ pa_status pa_alloc_prompt(pa_allocator* a, int64_t seq_id, int32_t num_tokens,
 /* Append n tokens.  If the last block is partly filled and shared, one fresh
  * block is taken first and (src, dst) is returned for a whole-block copy
  * (cow_src_dst[2], *num_cow = 1; else *num_cow = 0); then
- * ceil((L+n)/bs) - ceil(L/bs) new blocks.  slots_out: [n] or NULL. */
+ * ceil((L+n)/bs) - ceil(L/bs) new blocks.  slots_out: [n] or NULL.
+ * A sequence holds at most INT32_MAX tokens (lengths leave the allocator as
+ * int32): an append past that is PA_ERR_INVALID, here and in the batch call. */
 pa_status pa_append_tokens(pa_allocator* a, int64_t seq_id, int32_t n, int64_t* slots_out,
                            int32_t* cow_src_dst, int32_t* num_cow);
 
@@ -487,7 +489,8 @@ int32_t pa_buddy_size_for(int64_t num_tokens);
  * NULL) num_tokens slots in that size's view. */
 pa_status pa_buddy_alloc_prompt(pa_buddy_allocator* a, int64_t seq_id, int32_t num_tokens,
                                 int32_t block_size, int32_t* block_size_out, int64_t* slots_out);
-/* As pa_append_tokens, in the sequence's view. */
+/* As pa_append_tokens (the INT32_MAX-token limit included), in the
+ * sequence's view. */
 pa_status pa_buddy_append_tokens(pa_buddy_allocator* a, int64_t seq_id, int32_t n,
                                  int64_t* slots_out, int32_t* cow_src_dst, int32_t* num_cow);
 /* As pa_append_tokens_batch (sequences of any sizes; each row of slots_out

@@ -13,6 +13,7 @@
 //    state, so an error (including OOM) leaves the allocator unchanged;
 //  * a batch append for the decode step of many sequences, so one call does
 //    the per-step host work of a whole batch.
+#include <climits>
 #include <algorithm>
 #include <cstdint>
 #include <new>
@@ -94,6 +95,9 @@ pa_status pa_append_tokens(pa_allocator* a, int64_t seq_id, int32_t n, int64_t* 
   if (it == a->seqs.end())
     return pa::fail(PA_ERR_NO_SEQ, "pa_append_tokens: no sequence %lld", (long long)seq_id);
   Sequence& s = it->second;
+  if (s.len + n > INT32_MAX)   // lengths leave the allocator as int32
+    return pa::fail(PA_ERR_INVALID, "pa_append_tokens: sequence %lld would pass INT32_MAX tokens",
+                    (long long)seq_id);
   auto need_now = [&] {
     bool cow = false;
     return a->demand(s, n, s.table.empty() ? 0 : a->refs[s.table.back()], &cow);
@@ -129,6 +133,10 @@ pa_status pa_append_tokens_batch(pa_allocator* a, const int64_t* seq_ids, int32_
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end())
       return pa::fail(PA_ERR_NO_SEQ, "pa_append_tokens_batch: no sequence %lld",
+                      (long long)seq_ids[i]);
+    if (it->second.len + n > INT32_MAX)
+      return pa::fail(PA_ERR_INVALID,
+                      "pa_append_tokens_batch: sequence %lld would pass INT32_MAX tokens",
                       (long long)seq_ids[i]);
     listed[i] = &it->second;
   }

@@ -25,6 +25,7 @@
 //    copy-on-write of a shared, partly filled last block, taken before the
 //    growth blocks), all or nothing with the whole demand counted first.
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <new>
 #include <unordered_map>
@@ -241,6 +242,10 @@ pa_status pa_buddy_append_tokens(pa_buddy_allocator* a, int64_t seq_id, int32_t 
   if (it == a->seqs.end())
     return pa::fail(PA_ERR_NO_SEQ, "pa_buddy_append_tokens: no sequence %lld", (long long)seq_id);
   Seq& s = it->second;
+  if (s.len + n > INT32_MAX)   // lengths leave the allocator as int32
+    return pa::fail(PA_ERR_INVALID,
+                    "pa_buddy_append_tokens: sequence %lld would pass INT32_MAX tokens",
+                    (long long)seq_id);
   bool cow = false;
   const int32_t last_refs = s.table.empty() ? 0 : a->refs[int64_t(s.table.back()) << s.order];
   const int64_t need = a->demand(s, n, last_refs, &cow);
@@ -279,6 +284,10 @@ pa_status pa_buddy_append_tokens_batch(pa_buddy_allocator* a, const int64_t* seq
       auto it = a->seqs.find(seq_ids[i]);
       if (it == a->seqs.end())
         return pa::fail(PA_ERR_NO_SEQ, "pa_buddy_append_tokens_batch: no sequence %lld",
+                        (long long)seq_ids[i]);
+      if (it->second.len + n > INT32_MAX)
+        return pa::fail(PA_ERR_INVALID,
+                        "pa_buddy_append_tokens_batch: sequence %lld would pass INT32_MAX tokens",
                         (long long)seq_ids[i]);
       listed.push_back(&it->second);
     }

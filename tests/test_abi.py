@@ -210,3 +210,27 @@ def test_table_rows_wider_than_int32_tokens_are_refused():
     for pb in (-1, 257):
         assert pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 4, 33, pb) == 0
         assert _decode(p, maxb=33, pb=pb) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_sequences_stop_at_int32_max_tokens():
+    """Lengths leave the allocator as int32 (packed tables, length queries):
+    an append that would take a sequence past INT32_MAX tokens is refused,
+    single or batched, and leaves the allocator unchanged."""
+    h = ctypes.c_void_p()
+    assert pa.lib.pa_allocator_create(4096, 1 << 20, None, ctypes.byref(h)) == pa.PA_OK
+    try:
+        top = 2**31 - 1
+        assert pa.lib.pa_alloc_prompt(h, 7, top - 5, None) == pa.PA_OK    # 2048 blocks
+        free0 = pa.lib.pa_num_free_blocks(h)
+        assert pa.lib.pa_append_tokens(h, 7, 6, None, None, None) == pa.PA_ERR_INVALID
+        assert b"INT32_MAX" in pa.lib.pa_last_error()
+        ids = (ctypes.c_int64 * 1)(7)
+        assert pa.lib.pa_append_tokens_batch(h, ids, 1, 6, None, None, None) == pa.PA_ERR_INVALID
+        assert pa.lib.pa_num_free_blocks(h) == free0
+        assert pa.lib.pa_append_tokens(h, 7, 5, None, None, None) == pa.PA_OK   # exactly INT32_MAX
+        tab = (ctypes.c_int32 * 2048)()
+        ln = (ctypes.c_int32 * 1)()
+        assert pa.lib.pa_pack_block_tables(h, ids, 1, 2048, tab, ln) == pa.PA_OK
+        assert ln[0] == top
+    finally:
+        pa.lib.pa_allocator_destroy(h)
