@@ -243,8 +243,9 @@ hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream)
                          dim3(64), 0, stream, a, window);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0,
-                     stream, a);
+  const int64_t groups = (n + 255) / 256;
+  if (groups > 0x7fffffff) return hipErrorInvalidValue;   // the grid's x limit
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(unsigned(groups)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
