@@ -224,7 +224,9 @@ pa_status pa_decode_append(void* out, int32_t out_dtype, const void* q, int32_t 
  *                 block_size); 1 <= shared_blocks <= max_blocks_per_seq.  Not
  *                 checked on the device.
  * f16, bf16 and fp8 pools (PA_ERR_UNSUPPORTED for f32); q of the pool's
- * type, or f16 / bf16 for fp8 pools (the prefix pass runs on MFMA).  A
+ * type, or f16 / bf16 for fp8 pools (the prefix pass runs on MFMA).  Value
+ * range: the prefix pass has pa_prefill_chunk's bound on V (bf16 pools:
+ * |v| <= 65504, see there), which pa_decode does not have.  A
  * workspace is always needed:
  * pa_decode_shared_prefix_workspace_bytes(...).  Other arguments as pa_decode.
  */
@@ -282,6 +284,15 @@ pa_status pa_decode_multi(void* out, int32_t out_dtype, const void* q, int32_t q
  *                     scales, as in pa_decode; |v| * 2^8 must stay within the
  *                     fp16 range, |v| <= 255 * 448 * scale).  out_dtype f32 or
  *                     q_dtype.
+ *                     Value range of V: the P V product runs on fp16 inputs,
+ *                     so bf16 pools convert V to fp16 (RNE; exact for every
+ *                     bf16 value from 2^-14 to 65280).  Every |v| must be at
+ *                     most 65504: a larger value becomes inf, and that
+ *                     (head, dimension) of the output turns inf or NaN for
+ *                     every row that sees its key (and may for rows of the
+ *                     same key tile that do not).  Values below 2^-14 keep
+ *                     fp16's subnormal spacing (an absolute error of at most
+ *                     2^-25 per value).  Not checked.
  *   query_start_loc   device, [num_seqs + 1] int32, non-decreasing, from 0.
  *   context_lens      device, [num_seqs] int32, S_i <= L_i <=
  *                     max_blocks_per_seq * block_size (chunk included); the

@@ -48,31 +48,32 @@ def decode(codes):
     return _TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
+# Midpoints between neighbouring non-negative codes (exact in float64: each
+# is a value of the format with one more mantissa bit).
+_MIDPOINTS = (_POS_VALUES[:-1] + _POS_VALUES[1:]) / 2
+
+
 def encode(x):
     """float array -> uint8 codes: RNE to the nearest E4M3FN value, saturating.
 
-    NaN inputs encode to 0x7F (with the input's sign bit).  Vectorised over
-    the array, one comparison per step:
-      1. a = |x|; values at or above 448 take code 0x7E;
-      2. hi = first non-negative code whose value is >= a, lo = hi - 1;
-      3. pick the nearer of lo / hi, ties to the even code;
-      4. put the sign bit back.
+    NaN inputs encode to 0x7F (with the input's sign bit).  With a = |x|:
+      1. the nearest non-negative code is the number of midpoints below a
+         (codes are in increasing order of value, so a lies between the
+         values of that code and the next, nearer to the former exactly when
+         it is below their midpoint);
+      2. a value exactly on a midpoint is a tie: it goes to the even code of
+         the two (the count above gives the lower one);
+      3. beyond the last midpoint the count is 0x7E, so anything at or above
+         448 takes code 0x7E (saturation);
+      4. the sign bit is put back.
     """
     x = np.asarray(x, dtype=np.float64)
     neg = np.signbit(x)
     a = np.abs(x)
     nan = np.isnan(a)
-    a_clean = np.where(nan, 0.0, a)
-    sat = a_clean >= MAX_FINITE
-    a_in = np.where(sat, 0.0, a_clean)
-    hi = np.searchsorted(_POS_VALUES, a_in, side="left")  # 0..0x7E
-    exact = _POS_VALUES[hi] == a_in
-    lo = np.maximum(hi - 1, 0)
-    d_lo = a_in - _POS_VALUES[lo]
-    d_hi = _POS_VALUES[hi] - a_in
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo & 1) == 1))
-    code = np.where(exact, hi, np.where(pick_hi, hi, lo))
-    code = np.where(sat, 0x7E, code)
+    code = np.searchsorted(_MIDPOINTS, np.where(nan, 0.0, a), side="left")  # 0..0x7E
+    on_mid = _MIDPOINTS[np.minimum(code, _MIDPOINTS.size - 1)] == a
+    code = code + (on_mid & ((code & 1) == 1))
     code = np.where(nan, 0x7F, code)
     code = code | np.where(neg, 0x80, 0)
     return code.astype(np.uint8)

@@ -349,8 +349,15 @@ def pa_decode_append(out, q, pool, key_new, value_new, new_slots, block_tables, 
     new_slots [B] int64) and pa_decode, in one launch; key_new/value_new
     [B, H, D] of the pool's type."""
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
-    assert new_slots.dtype == torch.int64 and key_new.dtype == value_new.dtype
+    assert new_slots.dtype == torch.int64
     what = "pa_decode_append"
+    # The C call takes no type for the new rows: the kernel reads them in the
+    # element type of q (which, for f32 / f16 / bf16 pools, the library
+    # requires to be the pool's), so any other type would be read as rows of
+    # the wrong width.
+    if not (key_new.dtype == value_new.dtype == q.dtype):
+        raise ValueError(f"{what}: key_new ({key_new.dtype}) and value_new ({value_new.dtype}) "
+                         f"must have q's dtype ({q.dtype})")
     _on_device(what, pool.device, out, q, key_new, value_new, new_slots, block_tables,
                context_lens, workspace)
     B, maxb = block_tables.shape

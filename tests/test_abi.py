@@ -166,6 +166,16 @@ def test_binding_refuses_host_tensors_and_wrong_shapes():
                             0.1)
     with pytest.raises(ValueError, match="not on a GPU"):
         pa.pa_decode_shared_prefix(out, q, pool, tables, lens, 1, 0.1)
+    # the new rows of pa_decode_append are read in q's type (the pool's for
+    # 16-bit pools): rows of any other width are refused before the call
+    for bad in (torch.uint8, torch.float8_e4m3fn, torch.float32, torch.bfloat16):
+        kn = torch.zeros((3, 2, 128), dtype=bad)
+        with pytest.raises(ValueError, match="dtype"):
+            pa.pa_decode_append(out, q, pool, kn, kn, torch.zeros(3, dtype=torch.int64), tables,
+                                lens, 0.1)
+        with pytest.raises(ValueError, match="dtype"):
+            pa.pa_decode_append(out, q, pool, q, kn, torch.zeros(3, dtype=torch.int64), tables,
+                                lens, 0.1)
     # the checks themselves, on the host device
     dev = torch.device("cpu")
     with pytest.raises(ValueError, match="contiguous"):

@@ -58,7 +58,19 @@ def test_ties_go_to_even_and_saturation():
 
 
 def test_quantize_divides_in_float32():
-    x = np.array([1.0, 3.0, -7.5], dtype=np.float32)
+    """A worked case where the precision of the division decides the code.
+
+    x = 0x3CD9999A (0.026562500745...) and scale = 0.1f (0.100000001490...):
+    the exact quotient is 0.26562500298..., just above the midpoint 0.265625
+    between 0.25 (2^-2: exponent field 5, mantissa 0 -> code 0x28) and
+    0.28125 (2^-2 * 1.125 -> code 0x29), so it rounds up to 0x29.  Rounded
+    to float32 first, the quotient is exactly 0.265625, a tie, which goes
+    to the even code 0x28.  Stored data divides in float32, so 0x28."""
+    from fractions import Fraction
+    x = np.array([0x3CD9999A], dtype=np.uint32).view(np.float32)
     s = np.float32(0.1)
-    q = (x / s).astype(np.float64)                           # float32 quotient
-    assert np.array_equal(fp8.quantize_f32(x, s), fp8.encode(q))
+    exact = Fraction(float(x[0])) / Fraction(float(s))
+    assert Fraction(0.265625) < exact < Fraction(0.265625) + Fraction(1, 10**8)
+    assert fp8.quantize_f32(x, s)[0] == 0x28
+    assert fp8.encode(np.array([float(exact)]))[0] == 0x29      # the float64 quotient
+    assert fp8.quantize_f32(-x, s)[0] == 0xA8                    # sign bit only
