@@ -184,6 +184,30 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and results as pa_decode
+ * (bit for bit), without the workspace: the split-K scratch is a fixed
+ * array of PA_DECODE_NOALLOC_MAX_WORKSPACE bytes in device memory, one per
+ * GPU, held by every GPU the library runs on until the process ends.  Its
+ * address on a GPU is looked up on the first call that runs there (on the
+ * device of `stream`); no call allocates or frees anything.
+ *   A batch whose split-K needs more than that
+ *   (pa_decode_workspace_bytes(...) > PA_DECODE_NOALLOC_MAX_WORKSPACE) is
+ *   PA_ERR_UNSUPPORTED, before any launch; use pa_decode with a workspace.
+ *   Calls on one GPU share the array: two that overlap in time (different
+ *   streams with no ordering between them) race on it and give undefined
+ *   results.  Calls on one stream, or otherwise ordered, are safe; nothing
+ *   in the array needs clearing between calls.
+ */
+#define PA_DECODE_NOALLOC_MAX_WORKSPACE (32u << 20)
+pa_status pa_decode_noalloc(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                            const pa_pool* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, float scale, int32_t partition_blocks,
+                            hipStream_t stream);
+
+/*
  * pa_decode_append -- pa_reshape_and_cache of each sequence's new token,
  * then pa_decode, in one launch (same results, same cache contents).  The
  * new row belongs to position context_lens[i] - 1 of sequence i: the

@@ -27,6 +27,8 @@ PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_SEQ
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_POOL_STREAM_KV = 1
 PA_POOL_FP8_AUTO_SCALE = 2
+# bytes of the fixed split-K scratch array behind pa_decode_noalloc (per GPU)
+PA_DECODE_NOALLOC_MAX_WORKSPACE = 32 << 20
 
 _DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
           torch.float8_e4m3fn: PA_FP8_E4M3}
@@ -39,7 +41,7 @@ EXPORTS = [
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_auto_partition_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_chunk",
     "pa_decode_multi_workspace_bytes", "pa_decode_multi", "pa_decode_append",
-    "pa_decode_shared_prefix_workspace_bytes", "pa_decode_shared_prefix",
+    "pa_decode_shared_prefix_workspace_bytes", "pa_decode_shared_prefix", "pa_decode_noalloc",
     "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_prompt", "pa_append_tokens",
     "pa_append_tokens_batch", "pa_fork", "pa_free_seq", "pa_get_block_table",
     "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
@@ -79,6 +81,8 @@ def _load():
         "pa_decode_auto_partition_blocks": (I32, [P, I32, I32]),
         "pa_decode_workspace_bytes": (SZ, [P, I32, I32, I32]),
         "pa_decode": (I32, [VP, I32, VP, I32, P, VP, I32, VP, I32, ctypes.c_float, I32, VP, SZ, VP]),
+        "pa_decode_noalloc": (I32, [VP, I32, VP, I32, P, VP, I32, VP, I32, ctypes.c_float, I32,
+                                    VP]),
         "pa_decode_append": (I32, [VP, I32, VP, I32, P, VP, VP, VP, VP, I32, VP, I32,
                                    ctypes.c_float, I32, VP, SZ, VP]),
         "pa_decode_multi_workspace_bytes": (SZ, [P, pi32, I32, I32, I32]),
@@ -323,6 +327,25 @@ def pa_decode(out, q, pool, block_tables, context_lens, scale, partition_blocks=
                          _ptr(block_tables), maxb, _ptr(context_lens), B, float(scale),
                          int(partition_blocks), _ptr(workspace), ws_bytes,
                          _stream(stream, pool.device)), "pa_decode")
+
+
+def pa_decode_noalloc(out, q, pool, block_tables, context_lens, scale, partition_blocks=0,
+                      stream=None, q_dtype=None, out_dtype=None):
+    """pa_decode without a workspace argument: the library's fixed per-GPU
+    split-K array (PA_DECODE_NOALLOC_MAX_WORKSPACE bytes) serves instead, so
+    the call allocates nothing.  Calls that overlap on one GPU race on it."""
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    what = "pa_decode_noalloc"
+    _on_device(what, pool.device, out, q, block_tables, context_lens)
+    B, maxb = block_tables.shape
+    for name, t in (("q", q), ("out", out)):
+        _shape(what, name, t, (B, pool.num_heads, pool.head_dim))
+    _shape(what, "context_lens", context_lens, (B,))
+    _check(lib.pa_decode_noalloc(_ptr(out), dtype_code(out) if out_dtype is None else out_dtype,
+                                 _ptr(q), dtype_code(q) if q_dtype is None else q_dtype,
+                                 pool.ref(), _ptr(block_tables), maxb, _ptr(context_lens), B,
+                                 float(scale), int(partition_blocks),
+                                 _stream(stream, pool.device)), what)
 
 
 def pa_prefill_chunk(out, q, pool, block_tables, context_lens, query_start_loc, max_query_len,

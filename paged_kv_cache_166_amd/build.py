@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libpa.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["status.cpp", "allocator.cpp", "prefix.cpp", "buddy.cpp", "api.cpp", "cache_write.hip", "decode.hip",
-           "prefill.hip"]
+           "prefill.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -294,6 +294,33 @@ pa_status pa_decode(void* out, int32_t out_dtype, const void* q, int32_t q_dtype
                      partition_blocks, workspace, workspace_bytes, stream);
 }
 
+pa_status pa_decode_noalloc(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                            const pa_pool* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, float scale, int32_t partition_blocks,
+                            hipStream_t stream) {
+  const char* fn = "pa_decode_noalloc";
+  if (pa_status s = check_pool(fn, pool)) return s;
+  // Size first (no HIP call before it): a batch the array cannot hold is
+  // refused outright.  Arguments pa_decode would refuse give 0 here and are
+  // refused by decode_impl below.
+  const size_t need =
+      pa_decode_workspace_bytes(pool, num_seqs, max_blocks_per_seq, partition_blocks);
+  if (need > PA_DECODE_NOALLOC_MAX_WORKSPACE)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: this batch needs %zu bytes of split-K scratch, more than the %u of the "
+                "fixed array; use pa_decode with a workspace",
+                fn, need, PA_DECODE_NOALLOC_MAX_WORKSPACE);
+  void* ws = nullptr;
+  if (need > 0 && num_seqs > 0) {
+    if (pa_status s = hip_status(fn, pa::noalloc_scratch(stream, &ws))) return s;
+  }
+  return decode_impl(fn, out, out_dtype, q, q_dtype, pool, nullptr, nullptr, nullptr,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, scale,
+                     partition_blocks, ws, need > 0 ? size_t(PA_DECODE_NOALLOC_MAX_WORKSPACE) : 0,
+                     stream);
+}
+
 pa_status pa_decode_append(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
                            const pa_pool* pool, const void* key_new, const void* value_new,
                            const int64_t* new_slots, const int32_t* block_tables,

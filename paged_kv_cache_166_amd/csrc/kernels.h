@@ -133,4 +133,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int q_dtype, int h
 hipError_t launch_prefix_partials(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim,
                                   int block_size, hipStream_t stream);
 
+// Device address of the fixed split-K scratch of pa_decode_noalloc on the
+// GPU of `stream` (looked up once per GPU).
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 }  // namespace pa

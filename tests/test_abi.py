@@ -222,6 +222,32 @@ def test_table_rows_wider_than_int32_tokens_are_refused():
         assert _decode(p, maxb=33, pb=pb) == pa.PA_ERR_UNSUPPORTED
 
 
+def test_noalloc_refuses_batches_beyond_its_fixed_scratch():
+    """pa_decode_noalloc keeps its split-K scratch in a fixed array of
+    PA_DECODE_NOALLOC_MAX_WORKSPACE bytes: a batch that needs more is refused
+    with a clear error before any HIP call, one that fits passes the size
+    check (and then the ordinary argument checks)."""
+    def call(pool, B, maxb, pb):
+        return pa.lib.pa_decode_noalloc(ctypes.c_void_p(0x30000), pa.PA_F32, ctypes.c_void_p(0x40000),
+                                        pool.kv_dtype if pool.kv_dtype != pa.PA_FP8_E4M3 else pa.PA_BF16,
+                                        ctypes.byref(pool), ctypes.c_void_p(0x50000), maxb,
+                                        ctypes.c_void_p(0x60000), B, 0.1, pb, None)
+    p = _fake_pool(num_heads=40)
+    # 64 sequences x 40 heads x 128 partitions x (128 + 2) floats = 170 MB
+    need = pa.lib.pa_decode_workspace_bytes(ctypes.byref(p), 64, 4096, 32)
+    assert need > pa.PA_DECODE_NOALLOC_MAX_WORKSPACE
+    assert call(p, 64, 4096, 32) == pa.PA_ERR_UNSUPPORTED
+    msg = pa.lib.pa_last_error()
+    assert b"split-K scratch" in msg and str(need).encode() in msg
+    # the long fp8 decode workload's split (4 x 32 heads, 256 partitions) fits
+    p8 = _fake_pool(num_heads=32, block_size=32, kv_dtype=pa.PA_FP8_E4M3, k_scale=0x70000,
+                    v_scale=0x80000)
+    assert 0 < pa.lib.pa_decode_workspace_bytes(ctypes.byref(p8), 4, 4096, 16) \
+        <= pa.PA_DECODE_NOALLOC_MAX_WORKSPACE
+    # pool checks come first too
+    assert call(_fake_pool(block_size=12), 2, 4, 0) == pa.PA_ERR_UNSUPPORTED
+
+
 def test_sequences_stop_at_int32_max_tokens():
     """Lengths leave the allocator as int32 (packed tables, length queries):
     an append that would take a sequence past INT32_MAX tokens is refused,
