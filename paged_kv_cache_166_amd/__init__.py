@@ -64,14 +64,26 @@ class _Pool(ctypes.Structure):
                 ("kv_dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
+# PA_HOST_LIB names a host-only build of the allocator, prefix index and
+# buddy arena (build_host_san.py: ASan + UBSan, no HIP code) for the
+# sanitizer run of the host tests; the GPU calls are then absent and calling
+# one raises.  Unset, the full libpa.so is required.
+HOST_LIB = os.environ.get("PA_HOST_LIB")
+
+
 def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+    path = HOST_LIB or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run __graft_entry__.build() "
                           "(or python paged_kv_cache_166_amd/build.py)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     missing = [s for s in EXPORTS if not hasattr(lib, s)]
-    if missing:
-        raise ImportError(f"libpa.so lacks {missing}")
+    gpu_calls = [s for s in missing if not s.startswith(("pa_allocator", "pa_alloc", "pa_append",
+                                                          "pa_fork", "pa_free", "pa_get",
+                                                          "pa_pack", "pa_num", "pa_block",
+                                                          "pa_prefix", "pa_buddy", "pa_last"))]
+    if missing and not (HOST_LIB and missing == gpu_calls):
+        raise ImportError(f"{os.path.basename(path)} lacks {missing}")
     P, I32, I64, SZ, VP = (ctypes.POINTER(_Pool), ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                            ctypes.c_void_p)
     pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -130,6 +142,8 @@ def _load():
         "pa_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
+        if name in missing:
+            continue
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
