@@ -90,6 +90,22 @@ class Timer:
         return self.e0.elapsed_time(self.e1) * 1e-3
 
 
+def loop_seconds(call, n, warm=2):
+    """Mean duration of one call over n back-to-back calls on the current
+    stream, bracketed by one event pair (no event between launches: an event
+    record waits for the caches' write-back and would add its cost to every
+    launch it brackets)."""
+    for _ in range(warm):
+        call()
+    tm = Timer()
+    tm.start()
+    for _ in range(n):
+        call()
+    tm.stop()
+    torch.cuda.synchronize()
+    return tm.seconds() / n
+
+
 class Staging:
     """Per-step host->device inputs (slots, tables, lengths, copy pairs)
     packed into one pinned buffer and sent with one copy on the compute
@@ -247,17 +263,22 @@ class DecodeBench:
         if ncow:
             pairs = d["cow"][torch.from_numpy(h["cow"][:, 0] >= 0).to(self.device)].contiguous()
             self.cows += ncow
-        for li, pool in enumerate(self.pools):
-            if pairs is not None:
+        if pairs is not None:
+            for pool in self.pools:
                 pa.pa_copy_blocks(pool, pairs)
+        # 16-bit pools: one event pair around the step's layers, one launch
+        # (pa_decode_append: decode kernel + merge kernel) per layer back to
+        # back, so the mean launch is the bracket / layers with no event
+        # inside it.  fp8 pools (a cache write before each decode): the pair
+        # brackets one decode launch of a middle layer.
+        if timed and self.fused:
+            tm_all = Timer()
+            tm_all.start()
+        for li, pool in enumerate(self.pools):
             if not self.fused:
                 pa.pa_reshape_and_cache(pool, self.knew[(k + li) % 4], self.vnew[(k + li) % 4],
                                         d["slots"].view(-1))
-            # one launch per step carries the event pair (an event record
-            # waits for the caches to be written back, which would otherwise
-            # stall every layer): a middle layer, in the steady state -- the
-            # first layer after the step's upload runs a few us slower
-            timing = timed and li == len(self.pools) // 2
+            timing = timed and not self.fused and li == len(self.pools) // 2
             if timing:
                 tm = Timer()
                 tm.start()
@@ -271,6 +292,9 @@ class DecodeBench:
             if timing:
                 tm.stop()
                 self.ev.append(tm)
+        if timed and self.fused:
+            tm_all.stop()
+            self.ev.append(tm_all)
         if timed:
             self.step_bytes.append(self.decode_bytes(lens))
         self.last = (d, lens)
@@ -610,9 +634,10 @@ class DecodeBench:
         decoded two ways with the same inputs: pa_decode (every sequence
         reads the shared prefix itself) and pa_decode_shared_prefix (the
         prefix read once for the whole batch on MFMA, each sequence's own
-        blocks by the decode kernel, one merge).  Event-timed medians; GB/s
-        over the logical bytes (every sequence's full context) and over the
-        unique bytes (the prefix once)."""
+        blocks by the decode kernel, one merge).  Mean of back-to-back calls
+        under one event pair; GB/s over the logical bytes (every sequence's
+        full context) and over the unique bytes (the prefix once), and the
+        fraction of the HBM peak on the unique bytes."""
         lens = self.lens_now()
         t, ln = self.alloc.pack(self.ids, self.maxb)
         shared = pa.shared_prefix_blocks(t, ln, self.bs)
@@ -626,16 +651,7 @@ class DecodeBench:
         ws_sp = pa.shared_prefix_workspace(pool, self.B, self.maxb, shared, 0)
 
         def timed(call):
-            ts = []
-            for r in range(reps + 3):
-                tm = Timer()
-                tm.start()
-                call()
-                tm.stop()
-                torch.cuda.synchronize()
-                if r >= 3:
-                    ts.append(tm.seconds())
-            return float(np.median(ts))
+            return loop_seconds(call, reps, warm=3)
 
         fused, self.fused = self.fused, False
         logical = self.decode_bytes(lens)      # no new rows stored in these calls
@@ -647,7 +663,8 @@ class DecodeBench:
         res = {"shared_blocks": shared, "logical_bytes": logical, "unique_bytes": unique}
         for name, sec in (("pa_decode", sec_d), ("pa_decode_shared_prefix", sec_s)):
             res[name] = {"us": sec * 1e6, "logical_GBps": logical / sec / 1e9,
-                         "unique_GBps": unique / sec / 1e9}
+                         "unique_GBps": unique / sec / 1e9,
+                         "hbm_frac_unique": unique / sec / 1e9 / HBM_PEAK_GBS}
         res["speedup"] = sec_d / sec_s
         return res
 
@@ -668,13 +685,18 @@ class DecodeBench:
         new_rows = 2 * self.B * self.H * self.D * ELEM[self.kv] if self.fused else 0
         return kv + qo + tables + scales + new_rows
 
+    def launch_seconds(self):
+        """Mean launch time of each timed step (s): the layer-loop bracket
+        over the layers (fused), or the one bracketed launch."""
+        per = self.layers if self.fused else 1
+        return [t.seconds() / per for t in self.ev]
+
     def kernel_stats(self):
         """Mean pa_decode launch time (s) and mean algorithmic bytes per launch."""
-        times = [t.seconds() for t in self.ev]
-        return float(np.mean(times)), float(np.mean(self.step_bytes))
+        return float(np.mean(self.launch_seconds())), float(np.mean(self.step_bytes))
 
     def kernel_spread(self):
-        return spread([t.seconds() for t in self.ev])
+        return spread(self.launch_seconds())
 
     def workload_config(self):
         c = self.cfg
@@ -802,7 +824,7 @@ class PrefillBench:
     def fp8_series(self, reps=20):
         """The workload's launch over an fp8 E4M3 pool (codes drawn N(0, 40^2)
         with scale 1/40 per (block, head), so values are N(0,1)) with the same
-        bf16 queries, tables and lengths: event-timed median, causal TFLOP/s,
+        bf16 queries, tables and lengths: mean of back-to-back calls, causal TFLOP/s,
         and the K/V bytes (one byte per element)."""
         N, H, D, bs = self.N, self.H, self.D, self.bs
         pool = pa.PagedPool.empty(N, H, bs, D, "fp8", self.device)
@@ -822,22 +844,29 @@ class PrefillBench:
         t, ln = self.alloc.pack(ids, self.maxb)
         td, ld = torch.from_numpy(t).to(self.device), torch.from_numpy(ln).to(self.device)
         out = torch.empty_like(self.out)
-        ts = []
-        for r in range(reps + 3):
-            tm = Timer()
-            tm.start()
-            pa.pa_prefill_chunk(out, self.q, pool, td, ld, self.qsl, self.S, self.scale)
-            tm.stop()
-            torch.cuda.synchronize()
-            if r >= 3:
-                ts.append(tm.seconds())
+        sec = loop_seconds(lambda: pa.pa_prefill_chunk(out, self.q, pool, td, ld, self.qsl, self.S,
+                                                       self.scale), reps, warm=3)
         for sid in ids:
             self.alloc.free_seq(int(sid))
-        sec = float(np.median(ts))
         del pool
         return {"kv_dtype": "fp8", "q_dtype": "bf16", "us": sec * 1e6,
                 "TFLOPs": self.flops() / sec / 1e12,
                 "kv_bytes": 2 * H * D * sum(c + self.S for c in self.ctx)}
+
+    def loop_us(self, reps=20):
+        """The workload's launch (bf16 pool, the batch allocated once), mean
+        of back-to-back calls under one event pair, in us."""
+        ids = np.arange(self.next_id, self.next_id + self.B, dtype=np.int64)
+        self.next_id += self.B
+        for j, sid in enumerate(ids):
+            self.alloc.alloc_prompt(int(sid), self.ctx[j] + self.S)
+        t, ln = self.alloc.pack(ids, self.maxb)
+        td, ld = torch.from_numpy(t).to(self.device), torch.from_numpy(ln).to(self.device)
+        sec = loop_seconds(lambda: pa.pa_prefill_chunk(self.out, self.q, self.pool, td, ld,
+                                                       self.qsl, self.S, self.scale), reps)
+        for sid in ids:
+            self.alloc.free_seq(int(sid))
+        return sec * 1e6
 
     def hbm_bytes(self):
         """Algorithmic bytes of one launch: every context and chunk K/V row
@@ -976,19 +1005,29 @@ def main():
             log("bench: fp8 pool")
             res["fp8_pool"] = b.fp8_series()
     else:
-        kv_bytes = work                   # per launch (one layer)
+        kv_bytes = work                   # per launch (one layer), logical
         step_s = wall / args.steps
         res.update(metric=METRIC if args.workload == "llama13b_decode"
                    else f"pa_decode KV GB/s at the {args.workload} workload",
                    value=kv_bytes * b.layers / step_s / 1e9, unit="GB/s", dtype=b.kv)
-        ach = kv_bytes / kt / 1e9
+        # the HBM has to deliver each distinct row once: with a shared prefix
+        # (the same blocks in every table) the unique bytes are the basis,
+        # the logical ones (the prefix counted per sequence) are reported apart
+        hbm_bytes = b.unique_bytes(b.last[1]) if args.workload == "prefix_cow" else kv_bytes
+        ach = hbm_bytes / kt / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS,
                            "traffic": measured_traffic(args.workload, "decode_kernel"),
                            "kernel": ("pa_decode_append" if b.fused else "pa_decode")
                            + " (decode_kernel + decode_merge_kernel)",
                            "kernel_us": kt * 1e6, "kernel_us_spread": b.kernel_spread(),
-                           "bytes_per_launch": kv_bytes}
+                           "bytes_per_launch": hbm_bytes,
+                           "basis": "unique bytes" if args.workload == "prefix_cow"
+                           else "algorithmic bytes"}
+        if args.workload == "prefix_cow":
+            res["roofline"]["logical_bytes_per_launch"] = kv_bytes
+            res["roofline"]["logical_GBps"] = kv_bytes / kt / 1e9
+        assert res["roofline"]["frac"] <= 1.0, res["roofline"]
         res["hbm_frac_step"] = kv_bytes * b.layers / step_s / 1e9 / HBM_PEAK_GBS
         res["decode_tokens_per_s"] = b.B / step_s
         res["pa_decode_us_per_layer"] = kt * 1e6
@@ -1016,7 +1055,62 @@ def main():
         res["cpu_baseline"] = b.cpu_baseline()
     else:
         res["cpu_baseline"] = None
+    if args.workload == "llama13b_decode" and not args.no_extras:
+        del b
+        torch.cuda.empty_cache()
+        res["other_workloads"] = other_workloads(device)
     print(json.dumps(res), flush=True)
+
+
+def other_workloads(device, reps=20):
+    """The other full-size workloads, one launch configuration each, so that
+    the default line carries all of them: the chunked prefill (MFMA), the
+    131072-token fp8 decode (HBM) and the shared-prefix decode (HBM on the
+    unique bytes).  Kernel times are means of back-to-back launches under one
+    event pair (the fp8 decode: its bench steps, a cache write with scale
+    upkeep and then the decode, the event pair around the decode)."""
+    out = {}
+    log("bench: other workloads: chunked prefill")
+    p = PrefillBench(4, 2, device)
+    us = p.loop_us(reps)
+    fl = p.flops()
+    out["chunked_prefill"] = {
+        "kernel": "prefill_kernel (pa_prefill_chunk)", "kernel_us": us,
+        "flops_per_launch": fl, "TFLOPs": fl / us / 1e6,
+        "mfma_frac": fl / us / 1e6 / BF16_PEAK_TFLOPS, "peak_TFLOPs": BF16_PEAK_TFLOPS,
+        "hbm_bytes_per_launch": p.hbm_bytes(), "config": p.workload_config(),
+        "fp8_pool": p.fp8_series(reps)}
+    del p
+    torch.cuda.empty_cache()
+    log("bench: other workloads: long fp8 decode")
+    steps, warm = 6, 2
+    d = DecodeBench("long_fp8_decode", steps, warm, device)
+    for k in range(warm):
+        d.step(k, False)
+    for k in range(warm, warm + steps):
+        d.step(k, True)
+    torch.cuda.synchronize()
+    kt, nb = d.kernel_stats()
+    out["long_fp8_decode"] = {
+        "kernel": "pa_decode (decode_kernel + decode_merge_kernel), 256 partitions",
+        "kernel_us": kt * 1e6, "kernel_us_spread": d.kernel_spread(), "bytes_per_launch": nb,
+        "GBps": nb / kt / 1e9, "hbm_frac": nb / kt / 1e9 / HBM_PEAK_GBS,
+        "config": d.workload_config()}
+    del d
+    torch.cuda.empty_cache()
+    log("bench: other workloads: shared-prefix decode")
+    d = DecodeBench("prefix_cow", 4, 2, device)
+    for k in range(2):
+        d.step(k, False)
+    torch.cuda.synchronize()
+    sp = d.shared_prefix_series(reps)
+    sp["config"] = d.workload_config()
+    for name in ("pa_decode", "pa_decode_shared_prefix"):
+        assert sp[name]["hbm_frac_unique"] <= 1.0, sp
+    out["prefix_cow"] = sp
+    del d
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
