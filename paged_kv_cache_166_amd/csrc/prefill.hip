@@ -51,7 +51,6 @@ constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBM = kWaves * kQW;       // query rows per workgroup
 constexpr int kBN = 32;                 // keys per tile
 constexpr int kXcds = 8;
-constexpr int kPrefetch = 2;            // K/V tiles in flight ahead of the one consumed
 
 template <int KV>
 __device__ __forceinline__ f32x16_t mfma_qk(uint4 a, uint4 b, f32x16_t c) {
@@ -149,6 +148,21 @@ __device__ __forceinline__ float2 half_pair(float v) {
   return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// a ^ b with b uniform (v_xor_b32 with an SGPR operand).  With the lane
+// constant a redefined once per tile (redefine() below), an LDS offset that
+// is a lane constant XOR a per-step constant is rebuilt with one VALU
+// operation per use instead of being kept, per step, in a register of its
+// own (the compiler would hoist all of them out of the loop).
+__device__ __forceinline__ uint32_t xor_here(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(b), "v"(a));
+  return r;
+}
+
+// Makes v opaque to the compiler from here on (same value): expressions of
+// it computed after this point are not hoisted above it.
+__device__ __forceinline__ void redefine(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 typedef __attribute__((address_space(3))) void lds_t;
 
 // s_waitcnt immediate: all LDS / scalar-memory operations done, vector
@@ -166,35 +180,28 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS (gfx950
-// global_load_lds_dwordx4): lane i's bytes land at dst + 16 i; dst is
-// wave-uniform.
-__device__ __forceinline__ void load_lds16(const void* src, char* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_t*)dst, 16, 0, 0);
-}
-
-// At least three waves per SIMD (at most 168 VGPRs; 48 KiB of LDS fit three
-// workgroups per CU): the loop is latency-bound, and a third workgroup per
-// CU hides more of it than the registers the compiler gives up cost.  (fp16
-// with 4-token blocks, whose tile loads span two blocks, would spill at that
-// bound and keeps two.)
+// Occupancy: at least three waves per SIMD (at most 168 VGPRs; 32 KiB of
+// LDS per workgroup): the loop is latency-bound, and a third workgroup per
+// CU hides more of it than the registers the compiler gives up cost.
 // kPrefix: the shared-prefix partials of pa_decode_shared_prefix -- query
 // rows are the batch's decode queries (row r = sequence r), keys are one
 // chunk of the shared prefix (sequence 0's table), no causal mask, and the
 // workgroup writes (max, sum, unnormalised output) per row to the decode
 // workspace instead of the normalised output.
 // QT: the 16-bit type of q and of the Q K^T MFMAs (the pool's type for
-// 16-bit pools; f16 or bf16 for fp8 pools).  fp8 pools: the E4M3 codes of a
-// tile land in LDS raw, by DMA, and each wave converts the codes its DMA
-// brought to 16 bits (exactly: every E4M3 value is a bf16 and an fp16 value)
-// into the same swizzled row layout the 16-bit pools' DMA produces; the
-// per-(block, head) scales are applied to the scores (K) and to the weights
-// before the P V product (V), so the only added rounding is that of the
-// scaled weights to fp16.
+// 16-bit pools; f16 or bf16 for fp8 pools).
+// K/V tiles travel through registers: each wave loads its part of tile t+2
+// (global_load_dwordx4, one tile ahead of the LDS ring) while the workgroup
+// computes on tile t+1's predecessor, converts it in registers -- bf16 V to
+// fp16; fp8 E4M3 codes to 16 bits (exactly: every E4M3 value is a bf16 and
+// an fp16 value), K to QT and V to fp16 -- and stores it into the next LDS
+// stage (ds_write_b128) in the swizzled row layout the fragment reads use.
+// fp8 pools: the per-(block, head) scales are applied to the scores (K) and
+// to the weights before the P V product (V), so the only added rounding is
+// that of the scaled weights to fp16.
 template <int KV, int QT, int D, int BS, bool kPrefix = false>
 __global__ __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(KV == PA_FP8_E4M3 || (KV == PA_F16 && D == 128 && BS == 4)
-                                       ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu((KV == PA_F16 && D == 128 && BS == 4) ? 2 : 3)))
 void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   constexpr bool kFp8 = KV == PA_FP8_E4M3;
   constexpr int kRowBytes = D * 2;
@@ -213,23 +220,19 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   constexpr int kRawPieces = D / 16;                   // 16-byte pieces per raw row
   constexpr int kRawBlocksPerLoad = kRawRowsPerLoad > BS ? kRawRowsPerLoad / BS : 1;
   static_assert(!kFp8 || (kRawLoadsPerWave >= 1 && kRawBlocksPerLoad <= 4), "fp8 tile geometry");
-  // vector-memory ops per tile (K + V)
-  constexpr int kOpsPerTile = kFp8 ? kRawLoadsPerWave : 2 * kLoadsPerWave;
+  // 16-byte staging registers per lane (the wave's part of one tile)
+  constexpr int kStage = kFp8 ? kRawLoadsPerWave : 2 * kLoadsPerWave;
   constexpr int kKSteps = D / 16;
   constexpr int kDBlocks = D / 32;
-  constexpr int kP = kPrefetch;                        // tiles in flight ahead
   static_assert(kLoadsPerWave >= 1 && kBlocksPerLoad <= 2, "tile geometry");
 
-  // Three-stage rings (tiles t, t+1, t+2) of K and V tiles, each stage its
-  // own array: the stage is a compile-time constant in every access (the
-  // loop is unrolled by three), so the compiler can tell that a DMA still in
-  // flight writes another stage than the one being read and does not wait
-  // for it.  Rows are 16-byte-chunk XOR-swizzled so that fragment reads do
-  // not collide on banks: K row r keeps chunk c at c ^ swz_k(r), V at
-  // c ^ swz_v(r).  A transposing V read touches 4 chunks of each of 4
-  // consecutive rows per half-wave: swz_v moves those rows to distinct
-  // aligned groups of 4 chunks.
-  static_assert(kP == 2, "three-stage rings");
+  // Three-stage ring of K and V tiles (the one consumed, the next one, the
+  // one being filled), each stage its own array so that every access names
+  // a compile-time stage (the loop is unrolled by three).  Rows are 16-byte-chunk
+  // XOR-swizzled so that fragment reads do not collide on banks: K row r
+  // keeps chunk c at c ^ swz_k(r), V at c ^ swz_v(r).  A transposing V read
+  // touches 4 chunks of each of 4 consecutive rows per half-wave: swz_v
+  // moves those rows to distinct aligned groups of 4 chunks.
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes], lds_k1[kTileBytes],
       lds_k2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes], lds_v1[kTileBytes],
@@ -246,15 +249,6 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   };
   auto swz_k = [](int r) { return (r * kChunks / 16) % kChunks; };
   auto swz_v = [](int r) { return 4 * ((r * kChunks / 16) % (kChunks / 4)); };
-  // fp8 pools: raw stages [K codes | V codes] of each tile, linear rows.
-  constexpr int kRawStageBytes = kFp8 ? 2 * kRawTileBytes : 16;
-  __shared__ __attribute__((aligned(1024))) char lds_r0[kRawStageBytes], lds_r1[kRawStageBytes],
-      lds_r2[kRawStageBytes];
-  auto stage_r = [&](auto st) -> char* {
-    if constexpr (decltype(st)::value == 0) return lds_r0;
-    else if constexpr (decltype(st)::value == 1) return lds_r1;
-    else return lds_r2;
-  };
 
   // Work item: (pair = seq * H + head, query tile); pairs are dealt to XCDs
   // round robin by pair, the query tiles of a pair go to the same XCD, last
@@ -307,9 +301,12 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // constant address space so that the uniform lookups below are scalar
   // loads (a vector load here would make the wait for it also wait for every
   // DMA issued before it).
-  typedef const __attribute__((address_space(4))) int32_t const_i32;
-  const_i32* table = (const_i32*)(a.block_tables + int64_t(seq) * a.max_blocks_per_seq);
-  const int last_idx = (L - 1) / BS;
+  // Entries are read as unsigned (block ids are never negative): widening
+  // one to 64 bits is then free, and the compiler waits for a scalar load
+  // only where the entry is used, not right after issuing it.
+  typedef const __attribute__((address_space(4))) uint32_t const_u32;
+  const_u32* table = (const_u32*)(a.block_tables + int64_t(seq) * a.max_blocks_per_seq);
+  const int last_idx = int(unsigned(L - 1) / BS);
   const int64_t last_blk = table[last_idx];
   // fp8 pools: scales through the constant address space (scalar reads);
   // register v of a lane holds key 8 (v / 4) + 4 half + v % 4 of a tile, in
@@ -327,21 +324,23 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   const uint16_t* kpool = (const uint16_t*)a.k_cache;
   const uint16_t* vpool = (const uint16_t*)a.v_cache;
 
-  // Inside a tile a lane always loads the same row-in-tile and chunk, so its
-  // byte offset from the (block, head) base is fixed: only the block id
-  // changes from tile to tile -- and, for blocks longer than a tile, which
-  // part of the block the tile is (a uniform offset).
-  uint32_t off_k[kLoadsPerWave], off_v[kLoadsPerWave];
-#pragma unroll
-  for (int i = 0; i < kLoadsPerWave; ++i) {
-    const int row = (wave * kLoadsPerWave + i) * kRowsPerLoad + lane / kChunks;
-    const int pos = lane % kChunks;
-    off_k[i] = uint32_t(((row % BS) * D + (pos ^ swz_k(row)) * 8) * 2);
-    off_v[i] = uint32_t(((row % BS) * D + (pos ^ swz_v(row)) * 8) * 2);
-  }
   const int64_t tile_stride = int64_t(H) * BS * D * 2;   // bytes between blocks
   const char* kbase0 = (const char*)a.k_cache + int64_t(head) * BS * D * 2;
   const char* vbase0 = (const char*)a.v_cache + int64_t(head) * BS * D * 2;
+
+  // 16-bit pools: wave-load li = wave * kLoadsPerWave + i of a tile covers
+  // rows li * kRowsPerLoad + lane / kChunks; the lane loads 16-byte chunk
+  // lane % kChunks of its row (the same offset from the (block, head) base
+  // in every tile) and stores it at its swizzled place in the stage.
+  const int ld_pos = lane % kChunks;
+  uint32_t ld_off[kLoadsPerWave], st_k[kLoadsPerWave], st_v[kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int row = (wave * kLoadsPerWave + i) * kRowsPerLoad + lane / kChunks;
+    ld_off[i] = uint32_t(((row % BS) * D + ld_pos * 8) * 2);
+    st_k[i] = uint32_t(row * kRowBytes + (ld_pos ^ swz_k(row)) * 16);
+    st_v[i] = uint32_t(row * kRowBytes + (ld_pos ^ swz_v(row)) * 16);
+  }
 
   // fp8 pools: this wave's raw wave-loads (K or V, which wave-load of the
   // tile, the lane's row and 16-byte piece).
@@ -362,14 +361,15 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // (blk_hint), so that its latency hides behind the tile in between.
   constexpr int kWaveRows = kLoadsPerWave * kRowsPerLoad;
   constexpr bool kOneBlockPerWave = !kFp8 && kBlocksPerLoad == 1 && kWaveRows <= BS;
-  auto wave_blk = [&](int t) -> int64_t {
+  auto wave_blk = [&](int t) -> uint32_t {
     return table[__builtin_amdgcn_readfirstlane(
-        min(((t0 + t) * kBN + wave * kWaveRows) / BS, last_idx))];
+        min(int(unsigned((t0 + t) * kBN + wave * kWaveRows) / BS), last_idx))];
   };
 
-  // DMA of tile t: into K stage dk and V stage dv (16-bit pools), or raw
-  // into dr (fp8 pools).  blk_hint: wave_blk(t) where kOneBlockPerWave.
-  auto dma_tile = [&](int t, char* dk, char* dv, char* dr, int64_t blk_hint) {
+  // Loads of this wave's part of tile t into the staging registers.
+  // blk_hint: wave_blk(t) where kOneBlockPerWave.
+  u32x4_t stg[kStage];
+  auto load_tile = [&](int t, uint32_t blk_hint) {
     const int kb = (t0 + t) * kBN;
     if constexpr (kFp8) {
       // Per-lane addresses over at most kRawBlocksPerLoad blocks (scalar
@@ -378,7 +378,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
 #pragma unroll
       for (int j = 0; j < kRawLoadsPerWave; ++j) {
         const int row0 = raw_li[j] * kRawRowsPerLoad;
-        const int b0 = __builtin_amdgcn_readfirstlane((kb + row0) / BS);
+        const int b0 = __builtin_amdgcn_readfirstlane(int(unsigned(kb + row0) / BS));
         int64_t blks[kRawBlocksPerLoad];
 #pragma unroll
         for (int b = 0; b < kRawBlocksPerLoad; ++b)
@@ -390,11 +390,11 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
         if (in) {
 #pragma unroll
           for (int b = 0; b < kRawBlocksPerLoad; ++b)
-            if (key / BS == b0 + b) blk = blks[b];
+            if (int(unsigned(key) / BS) == b0 + b) blk = blks[b];
         }
-        const int64_t e = (blk * blk_stride + head_off + int64_t(keyc % BS) * D) + raw_piece * 16;
-        const char* src = (const char*)(raw_v[j] ? a.v_cache : a.k_cache) + e;
-        load_lds16(src, dr + (raw_v[j] ? kRawTileBytes : 0) + raw_li[j] * 1024);
+        const int64_t e =
+            (blk * blk_stride + head_off + int64_t(unsigned(keyc) % BS) * D) + raw_piece * 16;
+        stg[j] = *(const u32x4_t*)((const char*)(raw_v[j] ? a.v_cache : a.k_cache) + e);
       }
       return;
     }
@@ -405,10 +405,11 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int li = wave * kLoadsPerWave + i;
         const int64_t blk =
-            kOneBlockPerWave ? blk_hint
-                             : table[__builtin_amdgcn_readfirstlane((kb + li * kRowsPerLoad) / BS)];
-        load_lds16(kbase0 + blk * tile_stride + in_blk + off_k[i], dk + li * 1024);
-        load_lds16(vbase0 + blk * tile_stride + in_blk + off_v[i], dv + li * 1024);
+            kOneBlockPerWave
+                ? blk_hint
+                : table[__builtin_amdgcn_readfirstlane(int(unsigned(kb + li * kRowsPerLoad) / BS))];
+        stg[i] = *(const u32x4_t*)(kbase0 + blk * tile_stride + in_blk + ld_off[i]);
+        stg[kLoadsPerWave + i] = *(const u32x4_t*)(vbase0 + blk * tile_stride + in_blk + ld_off[i]);
       }
       return;
     }
@@ -419,44 +420,32 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     for (int i = 0; i < kLoadsPerWave; ++i) {
       const int li = wave * kLoadsPerWave + i;
       const int row0 = li * kRowsPerLoad;
-      const int b0 = __builtin_amdgcn_readfirstlane((kb + row0) / BS);
+      const int b0 = __builtin_amdgcn_readfirstlane(int(unsigned(kb + row0) / BS));
       const int64_t blk_a = table[__builtin_amdgcn_readfirstlane(min(b0, last_idx))];
       const int64_t blk_b =
           kBlocksPerLoad > 1 ? table[__builtin_amdgcn_readfirstlane(min(b0 + 1, last_idx))] : blk_a;
-      const int row = row0 + lane / kChunks;
-      const int pos = lane % kChunks;
-      const int key = kb + row;
+      const int key = kb + row0 + lane / kChunks;
       const bool in = key < L;
       const int keyc = in ? key : L - 1;
-      const int64_t blk = in ? (key / BS == b0 ? blk_a : blk_b) : last_blk;
-      const int64_t e = blk * blk_stride + head_off + int64_t(keyc % BS) * D;
-      load_lds16(kpool + e + (pos ^ swz_k(row)) * 8, dk + li * 1024);
-      load_lds16(vpool + e + (pos ^ swz_v(row)) * 8, dv + li * 1024);
+      const int64_t blk = in ? (int(unsigned(key) / BS) == b0 ? blk_a : blk_b) : last_blk;
+      const int64_t e =
+          blk * blk_stride + head_off + int64_t(unsigned(keyc) % BS) * D + ld_pos * 8;
+      stg[i] = *(const u32x4_t*)(kpool + e);
+      stg[kLoadsPerWave + i] = *(const u32x4_t*)(vpool + e);
     }
   };
 
-  // bf16 pools: the V chunks this wave's DMA brought into stage dv, to fp16
-  // in place (each lane converts the 16 bytes it loaded).  Called once the
-  // wave's DMA of that tile has landed, before the barrier that publishes it.
-  // (Inline assembly for the same reason as the transposing reads: the
-  // compiler would drain the next tile's DMA before reading this stage.)
-  // fp8 pools: the raw pieces this wave's DMA brought into stage st, 16
-  // codes per lane, to 16 bits (K: QT, V: fp16) in the converted stage's
-  // swizzled rows (two 16-byte chunks, 2 piece and 2 piece + 1, per lane).
-  auto own_fp8_convert = [&](auto st) {
+  // The staging registers (tile t+1) into stage st: bf16 V converted to
+  // fp16 (RNE); fp8 codes, 16 per lane, to 16 bits (K: QT, V: fp16) as two
+  // 16-byte chunks, 2 piece and 2 piece + 1, of the row.
+  auto store_tile = [&](auto st) {
     if constexpr (kFp8) {
-      const char* dr = stage_r(st);
 #pragma unroll
       for (int j = 0; j < kRawLoadsPerWave; ++j) {
-        const uint32_t ra = uint32_t(reinterpret_cast<uintptr_t>(
-                                (const __attribute__((address_space(3))) char*)dr)) +
-                            (raw_v[j] ? kRawTileBytes : 0) + raw_li[j] * 1024 + lane * 16;
-        u32x4_t w[1];
-        lds_read_b128_x<1>(ra, w);
         uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float2_t lo = fp8x2_lo(w[0][i]), hi = fp8x2_hi(w[0][i]);
+          const float2_t lo = fp8x2_lo(stg[j][i]), hi = fp8x2_hi(stg[j][i]);
           if (QT == PA_BF16 && !raw_v[j]) {
             // every E4M3 value is exact in bf16: its float32 bits, truncated
             h[2 * i] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
@@ -467,29 +456,19 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
           }
         }
         const int row = raw_row[j];
-        char* dst = raw_v[j] ? stage_v(st) : stage_k(st);
+        char* dst = (raw_v[j] ? stage_v(st) : stage_k(st)) + row * kRowBytes;
         const int sw = raw_v[j] ? swz_v(row) : swz_k(row);
-        const uint32_t da = uint32_t(reinterpret_cast<uintptr_t>(
-                                (__attribute__((address_space(3))) char*)dst)) + row * kRowBytes;
-        const u32x4_t c0 = {h[0], h[1], h[2], h[3]}, c1 = {h[4], h[5], h[6], h[7]};
-        const uint32_t a0 = da + ((2 * raw_piece) ^ sw) * 16;
-        const uint32_t a1 = da + ((2 * raw_piece + 1) ^ sw) * 16;
-        asm volatile("ds_write_b128 %0, %1" : : "v"(a0), "v"(c0) : "memory");
-        asm volatile("ds_write_b128 %0, %1" : : "v"(a1), "v"(c1) : "memory");
+        *(u32x4_t*)(dst + ((2 * raw_piece) ^ sw) * 16) = u32x4_t{h[0], h[1], h[2], h[3]};
+        *(u32x4_t*)(dst + ((2 * raw_piece + 1) ^ sw) * 16) = u32x4_t{h[4], h[5], h[6], h[7]};
       }
-    }
-  };
-
-  auto own_v_to_f16 = [&](char* dv) {
-    if constexpr (KV == PA_BF16) {
-      const uint32_t a0 =
-          uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dv)) +
-          wave * kLoadsPerWave * 1024 + lane * 16;
-      u32x4_t w[kLoadsPerWave];
-      lds_read_b128_x<kLoadsPerWave>(a0, w);
+    } else {
 #pragma unroll
-      for (int i = 0; i < kLoadsPerWave; ++i) w[i] = bf16x8_to_f16x8(w[i]);
-      lds_write_b128_x<kLoadsPerWave>(a0, w);
+      for (int i = 0; i < kLoadsPerWave; ++i) {
+        *(u32x4_t*)(stage_k(st) + st_k[i]) = stg[i];
+        u32x4_t v = stg[kLoadsPerWave + i];
+        if constexpr (KV == PA_BF16) v = bf16x8_to_f16x8(v);
+        *(u32x4_t*)(stage_v(st) + st_v[i]) = v;
+      }
     }
   };
 
@@ -502,11 +481,14 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // a compile-time part.
   const int vt_rl = 4 * half + (lane % 16) / 4;
   const int vt_cl = 2 * ((lane / 16) % 2) + (lane % 4) / 2;   // chunk within the group of 4
-  const int vt_lane = vt_rl * kRowBytes + 16 * vt_cl + 8 * (lane % 2);
+  // K fragment reads: chunk (2 kk + half) ^ swz_k(col) of row col, i.e. the
+  // lane's offset for kk = 0 XOR 32 kk (the chunk index's bit 0 is half).
+  const uint32_t k_lane0 = uint32_t(col * kRowBytes + ((half ^ swz_k(col)) << 4));
+  // Dimension block db adds 64 (db ^ vt_sq) bytes to the lane's offset;
+  // the lane part below bit 6 is zero there, so the offset is vt_lane0 ^ 64 db.
   const int vt_sq = swz_v(vt_rl) / 4;
-  int vt_db[kDBlocks];
-#pragma unroll
-  for (int db = 0; db < kDBlocks; ++db) vt_db[db] = vt_lane + 64 * (db ^ vt_sq);
+  const uint32_t vt_lane0 =
+      uint32_t(vt_rl * kRowBytes + 16 * vt_cl + 8 * (lane % 2) + 64 * vt_sq);
 
   f32x16_t o[kDBlocks];
 #pragma unroll
@@ -518,45 +500,51 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   const int my_lim = kPrefix ? L - 1 : ctx + my_row;   // last key it sees
   const int tile_lim = kPrefix ? L - 1 : ctx + wq0;    // last key every row of the wave sees
 
-  // Prologue: tiles 0 and 1 in flight (past the last tile, the last again).
+  // Prologue: tiles 0 and 1 into stages 0 and 1, tile 2 into the registers.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  const int t_1 = min(1, n_tiles - 1);
-  dma_tile(0, stage_k(S0{}), stage_v(S0{}), stage_r(S0{}), kOneBlockPerWave ? wave_blk(0) : 0);
-  dma_tile(t_1, stage_k(S1{}), stage_v(S1{}), stage_r(S1{}),
-           kOneBlockPerWave ? wave_blk(t_1) : 0);
-  // the table entry of the tile the next iteration issues
-  int64_t blk_next = kOneBlockPerWave ? wave_blk(min(2, n_tiles - 1)) : 0;
-  __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile 0 landed
-  own_v_to_f16(stage_v(S0{}));
-  own_fp8_convert(S0{});
+  load_tile(0, kOneBlockPerWave ? wave_blk(0) : 0);
+  store_tile(S0{});
+  if (n_tiles > 1) {
+    load_tile(1, kOneBlockPerWave ? wave_blk(1) : 0);
+    store_tile(S1{});
+  }
+  if (n_tiles > 2) load_tile(2, kOneBlockPerWave ? wave_blk(2) : 0);
+  // the table entry of the tile the next load is for
+  uint32_t blk_next = kOneBlockPerWave ? wave_blk(min(3, n_tiles - 1)) : 0;
   wg_barrier();
 
-  // One tile: issue tile t+2 (stage st+2), consume tile t (stage st), wait
-  // for this wave's part of tile t+1 and meet the other waves (after which
-  // all of tile t+1 is in LDS and nobody reads stage st any more).  Every
-  // iteration issues exactly one tile's DMA, so the waits are exact.
+  // One tile: consume tile t (stage st).  Once its Q K^T products are
+  // issued, store tile t+2 from the registers into stage st+2 (nobody reads
+  // it: its tile t-1 was consumed before the last barrier) and load tile t+3
+  // into the registers; the barrier at the end publishes tile t+1's stage
+  // (stored an iteration ago) and retires stage st.
+  auto stage_next = [&](auto st, int t) {
+    using Snn = std::integral_constant<int, (decltype(st)::value + 2) % 3>;
+    if (t + 2 < n_tiles) {
+      store_tile(Snn{});
+      if (t + 3 < n_tiles) {
+        load_tile(t + 3, blk_next);
+        if constexpr (kOneBlockPerWave) blk_next = wave_blk(min(t + 4, n_tiles - 1));
+      }
+    }
+  };
   auto iter = [&](auto st, int t) {
-    constexpr int s0 = decltype(st)::value;
-    using Sn = std::integral_constant<int, (s0 + 1) % 3>;
-    using Snn = std::integral_constant<int, (s0 + 2) % 3>;
     const int kb = (t0 + t) * kBN;
     const bool active = kb <= wave_last_key;
+    uint32_t k_lane = k_lane0, vt_lane = vt_lane0;
+    redefine(k_lane);
+    redefine(vt_lane);
     const char* kl = stage_k(st);
+    // chunk (2 kk + half) ^ swz_k(col) of row col: the lane's offset for
+    // kk = 0, XOR 32 kk
     auto kfrag = [&](int kk) {
-      return *(const uint4*)(kl + col * kRowBytes + ((2 * kk + half) ^ swz_k(col)) * 16);
+      return *(const uint4*)(kl + xor_here(k_lane, uint32_t(kk) << 5));
     };
-    // The first LDS read of the tile comes before the next DMA is issued:
-    // where the compiler cannot tell which stage an in-flight DMA writes
-    // (the loop header) it waits for all of them, and at this point that is
-    // only tile t+1, issued an iteration ago.
-    const uint4 kf0 = active ? kfrag(0) : make_uint4(0, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    dma_tile(min(t + 2, n_tiles - 1), stage_k(Snn{}), stage_v(Snn{}), stage_r(Snn{}), blk_next);
-    if constexpr (kOneBlockPerWave) blk_next = wave_blk(min(t + 3, n_tiles - 1));
-    __builtin_amdgcn_sched_barrier(0);
+    stage_next(st, t);
     if (active) {
+      const uint4 kf0 = kfrag(0);
       const char* vl = stage_v(st);
       // fp8 pools: the K and V scales of the tile's blocks (scalar reads,
       // issued before the MFMAs that they wait behind).
@@ -565,7 +553,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
 #pragma unroll
         for (int j = 0; j < kScaleBlocks; ++j) {
           const int64_t blk =
-              table[__builtin_amdgcn_readfirstlane(min((kb + j * BS) / BS, last_idx))];
+              table[__builtin_amdgcn_readfirstlane(min(int(unsigned(kb) / BS) + j, last_idx))];
           sk[j] = kscale_c[blk * H + head];
           sv[j] = vscale_c[blk * H + head];
         }
@@ -577,6 +565,14 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       s = mfma_qk<QT>(kf0, qf[0], s);
 #pragma unroll
       for (int kk = 1; kk < kKSteps; ++kk) s = mfma_qk<QT>(kfrag(kk), qf[kk], s);
+      // K fragment reads two ahead of the MFMAs that use them
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int kk = 0; kk < kKSteps - 2; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       // Register v of this lane holds key 8*(v/4) + 4*half + v%4 of the tile.
       // Scores stay unscaled here; c = scale*log2(e) > 0 is folded into the
       // exponent below.
@@ -623,9 +619,9 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         x[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, -m));
-        psum += x[v];
+        if constexpr (kFp8) psum += x[v];
       }
-      l += psum;
+      if constexpr (kFp8) l += psum;
       // P^T as B operands: k-step tt takes accumulator registers 8tt .. 8tt+7,
       // i.e. keys 16tt + 8*(e/4) + 4*half + e%4 for e = 0..7.
       uint4 pf[2];
@@ -640,6 +636,21 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
                             pack_f16(x[8 * tt + 2], x[8 * tt + 3]),
                             pack_f16(x[8 * tt + 4], x[8 * tt + 5]),
                             pack_f16(x[8 * tt + 6], x[8 * tt + 7]));
+      if constexpr (!kFp8) {
+        // 16-bit pools: the row sum of the fp16 weights the P V product
+        // uses (two per v_dot2_f32_f16, float32 accumulation), so the
+        // normaliser matches the rounded weights
+        const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+        float ps = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pf[tt].x), one, ps, false);
+          ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pf[tt].y), one, ps, false);
+          ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pf[tt].z), one, ps, false);
+          ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pf[tt].w), one, ps, false);
+        }
+        l += ps;
+      }
       // O^T += V^T P^T : A = V^T from the V rows by transposing reads, in
       // the same key order as P; two dimension blocks' operands per wait.
       const uint32_t vbase =
@@ -649,10 +660,10 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
 #pragma unroll
         for (int db0 = 0; db0 < kDBlocks; db0 += 2) {
           uint2 v[4];
-          v[0] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + vt_db[db0]);
-          v[1] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + vt_db[db0]);
-          v[2] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + vt_db[db0 + 1]);
-          v[3] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + vt_db[db0 + 1]);
+          v[0] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0) << 6));
+          v[1] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0) << 6));
+          v[2] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0 + 1) << 6));
+          v[3] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0 + 1) << 6));
           lds_wait_tr(v);
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
@@ -664,16 +675,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       pv_step(std::integral_constant<int, 0>{});
       pv_step(std::integral_constant<int, 1>{});
     }
-    __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerTile));   // tile t+1 landed
-    if (t + 1 < n_tiles) {
-      own_v_to_f16(stage_v(Sn{}));
-      own_fp8_convert(Sn{});
-    }
     wg_barrier();
   };
-  // The first iteration is peeled so that both edges into the loop come
-  // from the same stage (the same DMA in flight): the compiler's view of
-  // outstanding LDS writes then stays exact across the back edge.
   iter(S0{}, 0);
   for (int t = 1; t < n_tiles;) {
     iter(S1{}, t);
@@ -683,7 +686,6 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     iter(S0{}, t);
     ++t;
   }
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // Normalise and store: lane holds query my_row, dims 8*(v/4) + 4*half + v%4.
   const float2 lp = half_pair(l);
