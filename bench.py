@@ -230,6 +230,15 @@ class DecodeBench:
                   for _ in range(4)]
         self.out = torch.empty((self.B, self.H, self.D), dtype=tdt[self.qdt], device=device)
         self.ws = pa.decode_workspace(self.pool, self.B, self.maxb, self.pb)
+        # tables that begin with the same blocks (the shared-prefix workload):
+        # the step decodes with pa_decode_shared_prefix_append, the prefix
+        # read once for the whole batch
+        self.shared = 0
+        if self.fused and workload == "prefix_cow":
+            t, ln = self.alloc.pack(self.ids, self.maxb)
+            self.shared = pa.shared_prefix_blocks(t, ln + 1, self.bs)
+            self.ws_sp = pa.shared_prefix_workspace(self.pool, self.B, self.maxb, self.shared,
+                                                    self.pb)
         self.scale = 1 / math.sqrt(self.D)
         self.ev = []
         self.step_bytes = []
@@ -282,7 +291,12 @@ class DecodeBench:
             if timing:
                 tm = Timer()
                 tm.start()
-            if self.fused:
+            if self.shared:
+                pa.pa_decode_shared_prefix_append(
+                    self.out, self.q[(k + li) % 4], pool, self.knew[(k + li) % 4],
+                    self.vnew[(k + li) % 4], d["slots"].view(-1), d["tables"], d["lens"],
+                    self.shared, self.scale, self.pb, self.ws_sp)
+            elif self.fused:
                 pa.pa_decode_append(self.out, self.q[(k + li) % 4], pool, self.knew[(k + li) % 4],
                                     self.vnew[(k + li) % 4], d["slots"].view(-1), d["tables"],
                                     d["lens"], self.scale, self.pb, self.ws)
@@ -1018,8 +1032,11 @@ def main():
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS,
                            "traffic": measured_traffic(args.workload, "decode_kernel"),
-                           "kernel": ("pa_decode_append" if b.fused else "pa_decode")
-                           + " (decode_kernel + decode_merge_kernel)",
+                           "kernel": ("pa_decode_shared_prefix_append (prefill_kernel prefix "
+                                      "pass + decode_kernel with the merge fused)"
+                                      if getattr(b, "shared", 0) else
+                                      ("pa_decode_append" if b.fused else "pa_decode")
+                                      + " (decode_kernel + decode_merge_kernel)"),
                            "kernel_us": kt * 1e6, "kernel_us_spread": b.kernel_spread(),
                            "bytes_per_launch": hbm_bytes,
                            "basis": "unique bytes" if args.workload == "prefix_cow"
@@ -1099,11 +1116,24 @@ def other_workloads(device, reps=20):
     del d
     torch.cuda.empty_cache()
     log("bench: other workloads: shared-prefix decode")
-    d = DecodeBench("prefix_cow", 4, 2, device)
-    for k in range(2):
+    steps, warm = 8, 2
+    d = DecodeBench("prefix_cow", steps, warm, device)
+    for k in range(warm):
         d.step(k, False)
+    for k in range(warm, warm + steps):
+        d.step(k, True)
     torch.cuda.synchronize()
+    kt, logical = d.kernel_stats()
+    unique = d.unique_bytes(d.last[1])
     sp = d.shared_prefix_series(reps)
+    # the workload's decode step as the bench runs it: the new rows stored
+    # and the prefix read once (pa_decode_shared_prefix_append)
+    sp["step"] = {"call": "pa_decode_shared_prefix_append", "kernel_us": kt * 1e6,
+                  "kernel_us_spread": d.kernel_spread(), "unique_bytes": unique,
+                  "unique_GBps": unique / kt / 1e9,
+                  "hbm_frac_unique": unique / kt / 1e9 / HBM_PEAK_GBS,
+                  "logical_bytes": logical}
+    assert sp["step"]["hbm_frac_unique"] <= 1.0, sp["step"]
     sp["config"] = d.workload_config()
     for name in ("pa_decode", "pa_decode_shared_prefix"):
         assert sp[name]["hbm_frac_unique"] <= 1.0, sp

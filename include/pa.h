@@ -241,7 +241,9 @@ pa_status pa_decode_append(void* out, int32_t out_dtype, const void* q, int32_t 
  *      each chunk's (max, sum, unnormalised output) into the workspace;
  *   2. each sequence's own blocks after the prefix, split into partitions of
  *      partition_blocks (0: automatic) as in pa_decode, into the workspace;
- *   3. the merge of all of them.
+ *   3. the merge of all of them: by the workgroup of step 2 when every
+ *      sequence's own blocks fit one partition (max_blocks_per_seq -
+ *      shared_blocks <= the partition size), else by a third launch.
  *   shared_blocks  the first shared_blocks entries of every row of
  *                 block_tables are the same blocks, and every sequence's
  *                 context covers them (context_lens[i] >= shared_blocks *
@@ -263,6 +265,27 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
                                   int32_t num_seqs, int32_t shared_blocks, float scale,
                                   int32_t partition_blocks, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_decode_shared_prefix_append -- pa_decode_shared_prefix with the step's
+ * new K/V row of each sequence stored and attended in the same launch, as
+ * pa_decode_append does for pa_decode (same results and cache contents as
+ * pa_reshape_and_cache of those rows followed by pa_decode_shared_prefix).
+ *   key_new, value_new, new_slots  as in pa_decode_append; the new row's
+ *                 position context_lens[i] - 1 lies past the shared blocks
+ *                 (a row is never written into a shared block).
+ * Other arguments, workspace and errors as pa_decode_shared_prefix (f16 and
+ * bf16 pools; fp8 pools: PA_ERR_UNSUPPORTED).
+ */
+pa_status pa_decode_shared_prefix_append(void* out, int32_t out_dtype, const void* q,
+                                         int32_t q_dtype, const pa_pool* pool,
+                                         const void* key_new, const void* value_new,
+                                         const int64_t* new_slots, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t shared_blocks, float scale,
+                                         int32_t partition_blocks, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pa_decode_multi -- pa_decode of one batch whose sequences live in several

@@ -42,6 +42,7 @@ EXPORTS = [
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_chunk",
     "pa_decode_multi_workspace_bytes", "pa_decode_multi", "pa_decode_append",
     "pa_decode_shared_prefix_workspace_bytes", "pa_decode_shared_prefix", "pa_decode_noalloc",
+    "pa_decode_shared_prefix_append",
     "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_prompt", "pa_append_tokens",
     "pa_append_tokens_batch", "pa_fork", "pa_free_seq", "pa_get_block_table",
     "pa_pack_block_tables", "pa_num_free_blocks", "pa_block_refcount", "pa_allocator_stats",
@@ -101,6 +102,8 @@ def _load():
         "pa_decode_shared_prefix_workspace_bytes": (SZ, [P, I32, I32, I32, I32]),
         "pa_decode_shared_prefix": (I32, [VP, I32, VP, I32, P, VP, I32, VP, I32, I32,
                                           ctypes.c_float, I32, VP, SZ, VP]),
+        "pa_decode_shared_prefix_append": (I32, [VP, I32, VP, I32, P, VP, VP, VP, VP, I32, VP,
+                                                 I32, I32, ctypes.c_float, I32, VP, SZ, VP]),
         "pa_decode_multi": (I32, [VP, I32, VP, I32, P, I32, VP, pi32, pi32, VP, ctypes.c_float, I32,
                                   VP, SZ, VP]),
         "pa_prefill_chunk": (I32, [VP, I32, VP, I32, P, VP, I32, VP, VP, I32, I32, ctypes.c_float,
@@ -448,6 +451,34 @@ def pa_decode_shared_prefix(out, q, pool, block_tables, context_lens, shared_blo
                                        int(shared_blocks), float(scale), int(partition_blocks),
                                        _ptr(workspace), _ws_bytes(workspace),
                                        _stream(stream, pool.device)), "pa_decode_shared_prefix")
+
+
+def pa_decode_shared_prefix_append(out, q, pool, key_new, value_new, new_slots, block_tables,
+                                   context_lens, shared_blocks, scale, partition_blocks=0,
+                                   workspace=None, stream=None):
+    """pa_decode_shared_prefix with each sequence's new row (position L - 1,
+    at new_slots [B] int64) stored and attended in the same launch;
+    key_new/value_new [B, H, D] of q's type."""
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert new_slots.dtype == torch.int64
+    what = "pa_decode_shared_prefix_append"
+    if not (key_new.dtype == value_new.dtype == q.dtype):
+        raise ValueError(f"{what}: key_new ({key_new.dtype}) and value_new ({value_new.dtype}) "
+                         f"must have q's dtype ({q.dtype})")
+    _on_device(what, pool.device, out, q, key_new, value_new, new_slots, block_tables,
+               context_lens, workspace)
+    B, maxb = block_tables.shape
+    for name, t in (("q", q), ("out", out), ("key_new", key_new), ("value_new", value_new)):
+        _shape(what, name, t, (B, pool.num_heads, pool.head_dim))
+    _shape(what, "new_slots", new_slots, (B,))
+    _shape(what, "context_lens", context_lens, (B,))
+    if workspace is None:
+        workspace = shared_prefix_workspace(pool, B, maxb, shared_blocks, partition_blocks)
+    _check(lib.pa_decode_shared_prefix_append(
+        _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), pool.ref(), _ptr(key_new),
+        _ptr(value_new), _ptr(new_slots), _ptr(block_tables), maxb, _ptr(context_lens), B,
+        int(shared_blocks), float(scale), int(partition_blocks), _ptr(workspace),
+        _ws_bytes(workspace), _stream(stream, pool.device)), what)
 
 
 def _pool_array(pools):

@@ -345,13 +345,19 @@ size_t pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_
   return size_t(ws_layout_parts(pool, num_seqs, std::max(g.total_parts, 2)).bytes);
 }
 
-pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
-                                  const pa_pool* pool, const int32_t* block_tables,
-                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                  int32_t num_seqs, int32_t shared_blocks, float scale,
-                                  int32_t partition_blocks, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "pa_decode_shared_prefix";
+}  // extern "C"
+
+namespace {
+
+// pa_decode_shared_prefix, and pa_decode_shared_prefix_append when key_new
+// is not NULL.
+pa_status shared_prefix_impl(const char* fn, void* out, int32_t out_dtype, const void* q,
+                             int32_t q_dtype, const pa_pool* pool, const void* key_new,
+                             const void* value_new, const int64_t* new_slots,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t shared_blocks, float scale, int32_t partition_blocks,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (pa_status st = check_pool(fn, pool)) return st;
 
   if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "%s: num_seqs %d", fn, num_seqs);
@@ -387,6 +393,14 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
   if (!workspace || size_t(w.bytes) > workspace_bytes || !aligned(workspace, 256))
     return fail(PA_ERR_INVALID, "%s: workspace of %lld bytes, 256-byte aligned, is required", fn,
                 (long long)w.bytes);
+  if (key_new) {
+    if (pool->kv_dtype == PA_FP8_E4M3)
+      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 pools write new rows with pa_reshape_and_cache",
+                  fn);
+    if (!value_new || !new_slots) return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+    if (!aligned(key_new, 16) || !aligned(value_new, 16) || !aligned(new_slots, 8))
+      return fail(PA_ERR_INVALID, "%s: key_new/value_new must be 16-byte aligned", fn);
+  }
   char* ws = static_cast<char*>(workspace);
   float* ws_ml = reinterpret_cast<float*>(ws + w.ml_off);
   float* ws_acc = reinterpret_cast<float*>(ws + w.acc_off);
@@ -439,9 +453,46 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
   a.scale_log2 = scale_log2;
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
+  // every sequence's own blocks fit one partition: that workgroup merges
+  a.fuse_merge = g.suffix_parts <= 1 ? 1 : 0;
+  a.k_new = key_new;
+  a.v_new = value_new;
+  a.new_slots = key_new ? new_slots : nullptr;
   return hip_status(fn, pa::launch_decode(a, pool->kv_dtype, pool->head_dim, pool->block_size,
                                           (pool->flags & PA_POOL_STREAM_KV) != 0, num_seqs,
                                           stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                  const pa_pool* pool, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t shared_blocks, float scale,
+                                  int32_t partition_blocks, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return shared_prefix_impl("pa_decode_shared_prefix", out, out_dtype, q, q_dtype, pool, nullptr,
+                            nullptr, nullptr, block_tables, max_blocks_per_seq, context_lens,
+                            num_seqs, shared_blocks, scale, partition_blocks, workspace,
+                            workspace_bytes, stream);
+}
+
+pa_status pa_decode_shared_prefix_append(void* out, int32_t out_dtype, const void* q,
+                                         int32_t q_dtype, const pa_pool* pool,
+                                         const void* key_new, const void* value_new,
+                                         const int64_t* new_slots, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t shared_blocks, float scale,
+                                         int32_t partition_blocks, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  if (!key_new) return fail(PA_ERR_INVALID, "pa_decode_shared_prefix_append: key_new is NULL");
+  return shared_prefix_impl("pa_decode_shared_prefix_append", out, out_dtype, q, q_dtype, pool,
+                            key_new, value_new, new_slots, block_tables, max_blocks_per_seq,
+                            context_lens, num_seqs, shared_blocks, scale, partition_blocks,
+                            workspace, workspace_bytes, stream);
 }
 
 size_t pa_decode_multi_workspace_bytes(const pa_pool* pools, const int32_t* max_blocks_per_seq,

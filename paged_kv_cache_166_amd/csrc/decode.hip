@@ -192,6 +192,29 @@ constexpr int kMaxPartBlocks = 256;
 
 constexpr int default_max_loads(int bs) { return bs >= 64 ? 4 : 8; }
 
+// Output element d of (seq, head) from the shared prefix's partials (max,
+// sum, unnormalised output of partitions 0 .. prefix_parts - 1, written by
+// the prefix pass that ran before this launch) and one more partial (M, S,
+// A): the log-sum-exp merge, M' = max(M, m_c), S' = S 2^(M - M') + l_c
+// 2^(m_c - M'), likewise A.
+template <int D>
+__device__ __forceinline__ void merge_prefix_partials(const DecodeArgs& a, int seq, int head,
+                                                      int d, float M, float S, float A) {
+  const int64_t base = (int64_t(seq) * a.num_heads + head) * a.ws_parts;
+#pragma unroll 4
+  for (int c = 0; c < a.prefix_parts; ++c) {
+    const float mc = a.ws_ml[2 * (base + c)], lc = a.ws_ml[2 * (base + c) + 1];
+    const float xc = a.ws_acc[(base + c) * D + d];
+    const float Mn = fmaxf(M, mc);
+    const float fo = __builtin_amdgcn_exp2f(M - Mn), fn = __builtin_amdgcn_exp2f(mc - Mn);
+    S = S * fo + lc * fn;
+    A = A * fo + xc * fn;
+    M = Mn;
+  }
+  store_from_f32(a.out, (int64_t(seq) * a.num_heads + head) * D + d, a.out_dtype,
+                 S > 0.f ? A / S : 0.f);
+}
+
 // One workgroup's work: (head, sequence, partition) = blockIdx (x, y, z).
 // kAppend (16-bit and fp32 pools): the step's new K/V row of each sequence
 // (position L - 1) comes with the call; the workgroup of the last partition
@@ -240,7 +263,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const int nparts = nblocks > a.first_block
                          ? (nblocks - a.first_block + a.part_blocks - 1) / a.part_blocks
                          : 0;
-  if (part >= nparts) return;
+  if (part >= nparts) {
+    // a sequence with no blocks past the shared prefix: its output is the
+    // merge of the prefix's partials alone
+    if (a.fuse_merge && part == 0 && tid < D)
+      merge_prefix_partials<D>(a, seq, head, tid, kNoMax, 0.f, 0.f);
+    return;
+  }
   const int nb = min(a.part_blocks, nblocks - blk0);
   const bool row_ok = !G::kIdleGroups || grp < BS;
 
@@ -428,6 +457,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     if (tid < D) store_from_f32(a.out, out_off + tid, a.out_dtype, S > 0.f ? A / S : 0.f);
     return;
   }
+  if (a.fuse_merge) {  // this is the sequence's only partition past the prefix
+    if (tid < D) merge_prefix_partials<D>(a, seq, head, tid, M, S, A);
+    return;
+  }
 
   // Split-K: publish this partition's (max, sum, acc) for the merge kernel.
   const int64_t pidx = (int64_t(seq) * H + head) * a.ws_parts + a.prefix_parts + part;
@@ -582,7 +615,7 @@ hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_
     hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, false>), grid, dim3(kWaves * 64),
                        0, stream, a);
   }
-  if (a.max_parts > 1 || a.prefix_parts > 0) launch_merge<D>(a, num_seqs, stream);
+  if ((a.max_parts > 1 || a.prefix_parts > 0) && !a.fuse_merge) launch_merge<D>(a, num_seqs, stream);
   return hipGetLastError();
 }
 

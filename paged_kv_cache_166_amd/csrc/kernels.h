@@ -40,6 +40,11 @@ struct DecodeArgs {
   // partitions per (sequence, head) in the workspace (its stride): max_parts,
   // or more when other launches own some of them (prefix_parts)
   int32_t ws_parts;
+  // pa_decode_shared_prefix when every sequence's own blocks fit one
+  // partition: the workgroup of that partition (of partition 0 when there
+  // are none) merges the prefix's partials with its own and writes the
+  // output, so no merge launch follows.
+  int32_t fuse_merge;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int block_size,

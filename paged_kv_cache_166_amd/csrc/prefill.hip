@@ -180,9 +180,12 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Occupancy: at least three waves per SIMD (at most 168 VGPRs; 32 KiB of
+// Occupancy: at least three waves per SIMD (at most 168 VGPRs; 48 KiB of
 // LDS per workgroup): the loop is latency-bound, and a third workgroup per
-// CU hides more of it than the registers the compiler gives up cost.
+// CU hides more of it than the registers the compiler gives up cost.  (fp8
+// pools with blocks shorter than a tile, whose raw loads span several
+// blocks, and fp16 with 4-token blocks at head size 128 would spill at that
+// bound and keep two.)
 // kPrefix: the shared-prefix partials of pa_decode_shared_prefix -- query
 // rows are the batch's decode queries (row r = sequence r), keys are one
 // chunk of the shared prefix (sequence 0's table), no causal mask, and the
@@ -201,7 +204,7 @@ __device__ __forceinline__ void wg_barrier() {
 // that of the scaled weights to fp16.
 template <int KV, int QT, int D, int BS, bool kPrefix = false>
 __global__ __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu((KV == PA_F16 && D == 128 && BS == 4) ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(((KV == PA_FP8_E4M3 && BS < 32) || (KV == PA_F16 && D == 128 && BS == 4)) ? 2 : 3)))
 void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   constexpr bool kFp8 = KV == PA_FP8_E4M3;
   constexpr int kRowBytes = D * 2;
@@ -369,7 +372,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // Loads of this wave's part of tile t into the staging registers.
   // blk_hint: wave_blk(t) where kOneBlockPerWave.
   u32x4_t stg[kStage];
-  auto load_tile = [&](int t, uint32_t blk_hint) {
+  auto load_tile = [&](u32x4_t (&dst)[kStage], int t, uint32_t blk_hint) {
     const int kb = (t0 + t) * kBN;
     if constexpr (kFp8) {
       // Per-lane addresses over at most kRawBlocksPerLoad blocks (scalar
@@ -394,7 +397,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
         }
         const int64_t e =
             (blk * blk_stride + head_off + int64_t(unsigned(keyc) % BS) * D) + raw_piece * 16;
-        stg[j] = *(const u32x4_t*)((const char*)(raw_v[j] ? a.v_cache : a.k_cache) + e);
+        dst[j] = *(const u32x4_t*)((const char*)(raw_v[j] ? a.v_cache : a.k_cache) + e);
       }
       return;
     }
@@ -408,8 +411,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
             kOneBlockPerWave
                 ? blk_hint
                 : table[__builtin_amdgcn_readfirstlane(int(unsigned(kb + li * kRowsPerLoad) / BS))];
-        stg[i] = *(const u32x4_t*)(kbase0 + blk * tile_stride + in_blk + ld_off[i]);
-        stg[kLoadsPerWave + i] = *(const u32x4_t*)(vbase0 + blk * tile_stride + in_blk + ld_off[i]);
+        dst[i] = *(const u32x4_t*)(kbase0 + blk * tile_stride + in_blk + ld_off[i]);
+        dst[kLoadsPerWave + i] = *(const u32x4_t*)(vbase0 + blk * tile_stride + in_blk + ld_off[i]);
       }
       return;
     }
@@ -430,22 +433,22 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       const int64_t blk = in ? (int(unsigned(key) / BS) == b0 ? blk_a : blk_b) : last_blk;
       const int64_t e =
           blk * blk_stride + head_off + int64_t(unsigned(keyc) % BS) * D + ld_pos * 8;
-      stg[i] = *(const u32x4_t*)(kpool + e);
-      stg[kLoadsPerWave + i] = *(const u32x4_t*)(vpool + e);
+      dst[i] = *(const u32x4_t*)(kpool + e);
+      dst[kLoadsPerWave + i] = *(const u32x4_t*)(vpool + e);
     }
   };
 
   // The staging registers (tile t+1) into stage st: bf16 V converted to
   // fp16 (RNE); fp8 codes, 16 per lane, to 16 bits (K: QT, V: fp16) as two
   // 16-byte chunks, 2 piece and 2 piece + 1, of the row.
-  auto store_tile = [&](auto st) {
+  auto store_tile = [&](auto st, const u32x4_t (&src)[kStage]) {
     if constexpr (kFp8) {
 #pragma unroll
       for (int j = 0; j < kRawLoadsPerWave; ++j) {
         uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float2_t lo = fp8x2_lo(stg[j][i]), hi = fp8x2_hi(stg[j][i]);
+          const float2_t lo = fp8x2_lo(src[j][i]), hi = fp8x2_hi(src[j][i]);
           if (QT == PA_BF16 && !raw_v[j]) {
             // every E4M3 value is exact in bf16: its float32 bits, truncated
             h[2 * i] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
@@ -464,8 +467,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     } else {
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
-        *(u32x4_t*)(stage_k(st) + st_k[i]) = stg[i];
-        u32x4_t v = stg[kLoadsPerWave + i];
+        *(u32x4_t*)(stage_k(st) + st_k[i]) = src[i];
+        u32x4_t v = src[kLoadsPerWave + i];
         if constexpr (KV == PA_BF16) v = bf16x8_to_f16x8(v);
         *(u32x4_t*)(stage_v(st) + st_v[i]) = v;
       }
@@ -504,13 +507,23 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  load_tile(0, kOneBlockPerWave ? wave_blk(0) : 0);
-  store_tile(S0{});
-  if (n_tiles > 1) {
-    load_tile(1, kOneBlockPerWave ? wave_blk(1) : 0);
-    store_tile(S1{});
+  if constexpr (!kFp8) {
+    // tiles 0 and 1 in flight together (fp8 pools: one after the other, the
+    // second set of registers would spill there)
+    u32x4_t stg1[kStage];
+    load_tile(stg, 0, kOneBlockPerWave ? wave_blk(0) : 0);
+    if (n_tiles > 1) load_tile(stg1, 1, kOneBlockPerWave ? wave_blk(1) : 0);
+    store_tile(S0{}, stg);
+    if (n_tiles > 1) store_tile(S1{}, stg1);
+  } else {
+    load_tile(stg, 0, 0);
+    store_tile(S0{}, stg);
+    if (n_tiles > 1) {
+      load_tile(stg, 1, 0);
+      store_tile(S1{}, stg);
+    }
   }
-  if (n_tiles > 2) load_tile(2, kOneBlockPerWave ? wave_blk(2) : 0);
+  if (n_tiles > 2) load_tile(stg, 2, kOneBlockPerWave ? wave_blk(2) : 0);
   // the table entry of the tile the next load is for
   uint32_t blk_next = kOneBlockPerWave ? wave_blk(min(3, n_tiles - 1)) : 0;
   wg_barrier();
@@ -523,9 +536,9 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   auto stage_next = [&](auto st, int t) {
     using Snn = std::integral_constant<int, (decltype(st)::value + 2) % 3>;
     if (t + 2 < n_tiles) {
-      store_tile(Snn{});
+      store_tile(Snn{}, stg);
       if (t + 3 < n_tiles) {
-        load_tile(t + 3, blk_next);
+        load_tile(stg, t + 3, blk_next);
         if constexpr (kOneBlockPerWave) blk_next = wave_blk(min(t + 4, n_tiles - 1));
       }
     }

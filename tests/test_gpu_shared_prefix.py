@@ -141,3 +141,62 @@ def test_fp8_pool(qdt, D, bs):
                      pa.decode_workspace(sc.pool, len(seqs), t_dev.shape[1]))
         torch.cuda.synchronize()
         assert np.max(np.abs(got - plain.cpu().numpy())) < 1e-3
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+@pytest.mark.parametrize("bs", [4, 16, 64])
+def test_append_equals_write_then_shared_prefix(kv, bs):
+    """pa_decode_shared_prefix_append (the step's new rows stored and attended
+    in the launch) against pa_reshape_and_cache followed by
+    pa_decode_shared_prefix: bit for bit in the outputs and in the whole
+    pool, with the merge fused into the decode launch (automatic partitions)
+    and in its own launch (one-block partitions); and against the oracle.
+    One sequence has no tokens past the prefix before the step, one gets no
+    new row."""
+    from oracle import cache as C
+    from tests.gpu_util import bits_to_device, device_bits, to_bits
+    D, H = 128, 3
+    shared_blocks = max(1, 100 // bs)
+    own = [3, 0, 77, 200, 1, bs - 1]
+    sc = _batch(kv, D, bs, H, shared_blocks, own, seed=300 + bs)
+    seqs = list(range(len(own)))
+    slots = []
+    for i in seqs:
+        s_lib, cow = sc.alloc.append_tokens(i, 1)
+        s_ora, _ = sc.ora.append_tokens(i, 1)
+        assert list(s_lib) == s_ora and cow is None
+        slots += s_ora
+    slots[4] = -1                            # no new row for this one
+    rng = np.random.default_rng(bs)
+    kb = to_bits(rng.standard_normal((len(seqs), H, D), dtype=np.float32), kv)
+    vb = to_bits(rng.standard_normal((len(seqs), H, D), dtype=np.float32), kv)
+    kn, vn = bits_to_device(kb, kv, "cuda"), bits_to_device(vb, kv, "cuda")
+    sl = torch.tensor(slots, dtype=torch.int64, device="cuda")
+    q_dev, q64 = sc.random_q(len(seqs), kv)
+    t_dev, ln_dev, t, ln = sc.device_tables(seqs)
+    assert pa.shared_prefix_blocks(t, ln, bs) >= shared_blocks
+    scale = 1 / math.sqrt(D)
+    base_k, base_v = sc.pool.k_cache.clone(), sc.pool.v_cache.clone()
+    C.write_rows(sc.ok, kb, slots, bs)
+    C.write_rows(sc.ov, vb, slots, bs)
+    ref = _oracle(sc, seqs, q64, scale)
+    for pb in (0, 1):
+        outs, pools = [], []
+        for fused in (False, True):
+            sc.pool.k_cache.copy_(base_k)
+            sc.pool.v_cache.copy_(base_v)
+            out = torch.full(q_dev.shape, float("nan"), dtype=torch.float32, device="cuda")
+            if fused:
+                pa.pa_decode_shared_prefix_append(out, q_dev, sc.pool, kn, vn, sl, t_dev, ln_dev,
+                                                  shared_blocks, scale, pb)
+            else:
+                pa.pa_reshape_and_cache(sc.pool, kn, vn, sl)
+                pa.pa_decode_shared_prefix(out, q_dev, sc.pool, t_dev, ln_dev, shared_blocks,
+                                           scale, pb)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+            pools.append((device_bits(sc.pool.k_cache), device_bits(sc.pool.v_cache)))
+        assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), f"pb={pb}"
+        assert np.array_equal(pools[0][0], pools[1][0]) and np.array_equal(pools[0][1], pools[1][1])
+        assert np.array_equal(pools[1][0], sc.ok) and np.array_equal(pools[1][1], sc.ov)
+        assert_close(outs[1].astype(np.float64), ref, TOL[kv], f"{kv} bs={bs} pb={pb}")
