@@ -157,7 +157,7 @@ class DecodeBench:
     layer's pool and pa_decode over it."""
 
     def __init__(self, workload, steps, warmup, device, partition_blocks=None, layers=None,
-                 stream_kv=None):
+                 stream_kv=None, fused=None):
         self.name = workload
         cfg = W.CONFIGS[workload]
         self.cfg = cfg
@@ -195,9 +195,10 @@ class DecodeBench:
         self.stream_kv = (workload != "prefix_cow") if stream_kv is None else stream_kv
         # fp8: the step's appended tokens keep each block's scale at its amax / 448
         self.auto_scale = self.kv == "fp8"
-        # 16-bit pools: the step's new rows are stored by the decode launch
-        # itself (pa_decode_append); fp8 pools write them first (scale upkeep)
-        self.fused = self.kv != "fp8"
+        # the step's new rows are stored by the decode launch itself
+        # (pa_decode_append; fp8 pools quantise them there, with scale upkeep),
+        # or (fused=False) written by pa_reshape_and_cache first
+        self.fused = True if fused is None else fused
         self.lens0 = lens0
         self.alloc = pa.Allocator(self.N, self.bs, W.free_order(cfg["seed"], self.N))
         g = torch.Generator(device=device)

@@ -213,9 +213,13 @@ pa_status pa_decode_noalloc(void* out, int32_t out_dtype, const void* q, int32_t
  * new row belongs to position context_lens[i] - 1 of sequence i: the
  * workgroup that covers that position stores the row at new_slots[i] and
  * uses it from registers, so the row is never read back in this call.
- *   key_new, value_new  device, [num_seqs][num_heads][head_dim] of the pool's
- *                 KV type (f32, f16 or bf16 pools; fp8 pools: PA_ERR_UNSUPPORTED,
- *                 their rows go through pa_reshape_and_cache), 16-byte aligned.
+ *   key_new, value_new  device, [num_seqs][num_heads][head_dim] of q_dtype
+ *                 (which is the pool's type for f32, f16 and bf16 pools),
+ *                 16-byte aligned.  fp8 pools quantise them on the way in as
+ *                 pa_reshape_and_cache does: with PA_POOL_FP8_AUTO_SCALE the
+ *                 block's scale is kept up (its earlier rows requantised in
+ *                 the launch when it grows, and attended as requantised),
+ *                 else the block's scale is used as it is.
  *   new_slots     device, [num_seqs] int64: the slot of position
  *                 context_lens[i] - 1 (what pa_append_tokens returned);
  *                 < 0: no row for that sequence (nothing stored, the cache is
@@ -274,8 +278,8 @@ pa_status pa_decode_shared_prefix(void* out, int32_t out_dtype, const void* q, i
  *   key_new, value_new, new_slots  as in pa_decode_append; the new row's
  *                 position context_lens[i] - 1 lies past the shared blocks
  *                 (a row is never written into a shared block).
- * Other arguments, workspace and errors as pa_decode_shared_prefix (f16 and
- * bf16 pools; fp8 pools: PA_ERR_UNSUPPORTED).
+ * Other arguments, workspace and errors as pa_decode_shared_prefix (f16, bf16
+ * and fp8 pools, the new rows of fp8 pools quantised as in pa_decode_append).
  */
 pa_status pa_decode_shared_prefix_append(void* out, int32_t out_dtype, const void* q,
                                          int32_t q_dtype, const pa_pool* pool,

@@ -265,15 +265,13 @@ pa_status decode_impl(const char* fn, void* out, int32_t out_dtype, const void* 
   a.q_dtype = q_dtype;
   a.out_dtype = out_dtype;
   if (key_new) {
-    if (pool->kv_dtype == PA_FP8_E4M3)
-      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 pools write new rows with pa_reshape_and_cache",
-                  fn);
     if (!value_new || !new_slots) return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
     if (!aligned(key_new, 16) || !aligned(value_new, 16) || !aligned(new_slots, 8))
       return fail(PA_ERR_INVALID, "%s: key_new/value_new must be 16-byte aligned", fn);
     a.k_new = key_new;
     a.v_new = value_new;
     a.new_slots = new_slots;
+    a.fp8_upkeep = (pool->flags & PA_POOL_FP8_AUTO_SCALE) != 0;
   }
   return hip_status(fn, pa::launch_decode(a, pool->kv_dtype, pool->head_dim, pool->block_size,
                                           (pool->flags & PA_POOL_STREAM_KV) != 0, num_seqs,
@@ -394,9 +392,6 @@ pa_status shared_prefix_impl(const char* fn, void* out, int32_t out_dtype, const
     return fail(PA_ERR_INVALID, "%s: workspace of %lld bytes, 256-byte aligned, is required", fn,
                 (long long)w.bytes);
   if (key_new) {
-    if (pool->kv_dtype == PA_FP8_E4M3)
-      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 pools write new rows with pa_reshape_and_cache",
-                  fn);
     if (!value_new || !new_slots) return fail(PA_ERR_INVALID, "%s: NULL argument", fn);
     if (!aligned(key_new, 16) || !aligned(value_new, 16) || !aligned(new_slots, 8))
       return fail(PA_ERR_INVALID, "%s: key_new/value_new must be 16-byte aligned", fn);
@@ -458,6 +453,7 @@ pa_status shared_prefix_impl(const char* fn, void* out, int32_t out_dtype, const
   a.k_new = key_new;
   a.v_new = value_new;
   a.new_slots = key_new ? new_slots : nullptr;
+  a.fp8_upkeep = (pool->flags & PA_POOL_FP8_AUTO_SCALE) != 0;
   return hip_status(fn, pa::launch_decode(a, pool->kv_dtype, pool->head_dim, pool->block_size,
                                           (pool->flags & PA_POOL_STREAM_KV) != 0, num_seqs,
                                           stream));

@@ -35,19 +35,6 @@ __device__ __forceinline__ void load8_f32(const void* p, int dt, float* x) {
   }
 }
 
-// x / s rounded once in float32, then RNE to E4M3FN saturating at +-448.
-// Clamping first is exact: every |x/s| >= 448 rounds to 448 when saturating.
-__device__ __forceinline__ float fp8_prep(float x, float s) {
-  const float y = __fdiv_rn(x, s);
-  return __builtin_isnan(y) ? y : fminf(fmaxf(y, -448.f), 448.f);
-}
-
-__device__ __forceinline__ uint32_t pack4_fp8(const float* y) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-  return (uint32_t)w;
-}
-
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
   const int chunks = a.head_dim / 8;
   const int64_t n = int64_t(a.num_tokens) * a.num_heads * chunks;
@@ -88,17 +75,6 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = fp8_prep(x[i], vscale);
   *(uint2*)((uint8_t*)a.v_cache + dst_e) = make_uint2(pack4_fp8(y), pack4_fp8(y + 4));
-}
-
-// Eight codes requantised from scale s_old to divisor d:
-// RNE-saturate((decode(code) * s_old) / d), both steps rounded in float32.
-__device__ __forceinline__ uint2 requant8(uint2 w, float s_old, float d) {
-  float y[8];
-  const float2_t a0 = fp8x2_lo(w.x), a1 = fp8x2_hi(w.x), b0 = fp8x2_lo(w.y), b1 = fp8x2_hi(w.y);
-  const float x[8] = {a0.x, a0.y, a1.x, a1.y, b0.x, b0.y, b1.x, b1.y};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = fp8_prep(__fmul_rn(x[i], s_old), d);
-  return make_uint2(pack4_fp8(y), pack4_fp8(y + 4));
 }
 
 // Largest value over the 64 lanes of a wave.

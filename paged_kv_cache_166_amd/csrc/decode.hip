@@ -197,6 +197,64 @@ constexpr int default_max_loads(int bs) { return bs >= 64 ? 4 : 8; }
 // the prefix pass that ran before this launch) and one more partial (M, S,
 // A): the log-sum-exp merge, M' = max(M, m_c), S' = S 2^(M - M') + l_c
 // 2^(m_c - M'), likewise A.
+// 16 codes requantised from scale s_old to divisor d (see requant8).
+__device__ __forceinline__ uint4 requant16(uint4 w, float s_old, float d) {
+  const uint2 a = requant8(make_uint2(w.x, w.y), s_old, d);
+  const uint2 b = requant8(make_uint2(w.z, w.w), s_old, d);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// A new row stored into an fp8 pool from the decode launch: codes (16 per
+// lane, this lane's part of the row), the block's scale before (s_old) and
+// after (s_new) the row, the divisor of the quantisation, and whether the
+// block's earlier rows are requantised.  Without scale upkeep the row is
+// quantised with the block's scale, which stays.  With it (the same float32
+// operations as pa_reshape_and_cache's upkeep write, one-row runs): s_run =
+// amax(|row|) / 448, s_old = 0 when the row starts its block (position 0),
+// else the block's scale, s_new = max(s_old, s_run), divisor s_new (1 while
+// it is 0), the earlier rows requantised when s_new > s_old.  A row of 128
+// elements spans kLpr lanes; each of the wave's groups of kLpr lanes holds
+// the whole row, so the amax is a group maximum.
+struct Fp8Row {
+  uint4 codes;
+  float s_old, s_new, div;
+  bool requant;
+};
+
+template <int kLpr>
+__device__ __forceinline__ Fp8Row fp8_new_row(const void* src, int64_t off, int in_dtype,
+                                              const float* scale, int p, int upkeep) {
+  float x[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) x[e] = load_as_f32(src, off + e, in_dtype);
+  Fp8Row r;
+  const float s_cur = *scale;
+  if (upkeep) {
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+    for (int m = 1; m < kLpr; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    r.s_old = p == 0 ? 0.f : s_cur;
+    r.s_new = fmaxf(r.s_old, __fdiv_rn(amax, 448.f));
+    r.div = r.s_new > 0.f ? r.s_new : 1.f;
+    r.requant = p > 0 && r.s_new > r.s_old;
+  } else {
+    r.s_old = r.s_new = r.div = s_cur;
+    r.requant = false;
+  }
+  // the same in every lane: keep them in scalar registers
+  r.s_old = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, r.s_old)));
+  r.s_new = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, r.s_new)));
+  r.div = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, r.div)));
+  r.requant = __builtin_amdgcn_readfirstlane(int(r.requant)) != 0;
+  float y[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) y[e] = fp8_prep(x[e], r.div);
+  r.codes = make_uint4(pack4_fp8(y), pack4_fp8(y + 4), pack4_fp8(y + 8), pack4_fp8(y + 12));
+  return r;
+}
+
 template <int D>
 __device__ __forceinline__ void merge_prefix_partials(const DecodeArgs& a, int seq, int head,
                                                       int d, float M, float S, float A) {
@@ -279,12 +337,30 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // for these loads before any tile load could go out).
   uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
   int64_t new_slot = -1;
+  // fp8 pools: the new row's block and position in it, the scales before
+  // (s_old) and after (s_new) the row, the divisors of its quantisation, and
+  // whether the block's earlier rows are requantised (scale upkeep).
+  Fp8Row fk{}, fv{};
+  int64_t new_blk = -1;
+  int new_p = 0;
   if constexpr (kAppend) {
     if (part == nparts - 1 && wave == (nb - 1) % NW) new_slot = a.new_slots[seq];
     if (new_slot >= 0) {
-      const int64_t off = (out_off + col * E) * G::kElem;
-      knew = *(const uint4*)((const char*)a.k_new + off);
-      vnew = *(const uint4*)((const char*)a.v_new + off);
+      if constexpr (KV == PA_FP8_E4M3) {
+        new_blk = new_slot / BS;
+        new_p = int(new_slot % BS);
+        const int64_t si = new_blk * H + head;
+        fk = fp8_new_row<G::kLpr>(a.k_new, out_off + col * E, a.q_dtype, a.k_scale + si, new_p,
+                                  a.fp8_upkeep);
+        fv = fp8_new_row<G::kLpr>(a.v_new, out_off + col * E, a.q_dtype, a.v_scale + si, new_p,
+                                  a.fp8_upkeep);
+        knew = fk.codes;
+        vnew = fv.codes;
+      } else {
+        const int64_t off = (out_off + col * E) * G::kElem;
+        knew = *(const uint4*)((const char*)a.k_new + off);
+        vnew = *(const uint4*)((const char*)a.v_new + off);
+      }
     }
   }
   const bool has_new = new_slot >= 0;
@@ -296,8 +372,34 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const int n_w = wave < nb ? (nb - wave + NW - 1) / NW : 0;
   const int n_u = n_w * G::kSubs;
   const int64_t blk_stride = int64_t(H) * G::kTileBytes;
-  const char* kbase = (const char*)a.k_cache + int64_t(head) * G::kTileBytes + lane * 16;
-  const char* vbase = (const char*)a.v_cache + int64_t(head) * G::kTileBytes + lane * 16;
+  char* const kbase = (char*)a.k_cache + int64_t(head) * G::kTileBytes + lane * 16;
+  char* const vbase = (char*)a.v_cache + int64_t(head) * G::kTileBytes + lane * 16;
+
+  // fp8 scale upkeep: when the new row grows its block's scale, the block's
+  // earlier rows are requantised in place before the loop reads them.  Each
+  // lane rewrites exactly the 16 bytes it loads from that block in the loop,
+  // so its own later loads see the new codes (same lane, program order).
+  if constexpr (kAppend && KV == PA_FP8_E4M3) {
+    if (has_new && (fk.requant || fv.requant)) {
+#pragma unroll
+      for (int sub = 0; sub < G::kSubs; ++sub)
+#pragma unroll
+        for (int i = 0; i < G::kLoads; ++i) {
+          const int row = sub * G::kSubRows + i * G::kRows + grp;
+          if (row_ok && row < new_p) {
+            const int64_t off = new_blk * blk_stride + sub * G::kSubBytes + i * 1024;
+            if (fk.requant) {
+              uint4* kp = (uint4*)(kbase + off);
+              *kp = requant16(*kp, fk.s_old, fk.div);
+            }
+            if (fv.requant) {
+              uint4* vp = (uint4*)(vbase + off);
+              *vp = requant16(*vp, fv.s_old, fv.div);
+            }
+          }
+        }
+    }
+  }
 
   float m = kNoMax, l = 0.f;
   float acc[E];
@@ -338,14 +440,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   auto consume = [&](uint4* kr, uint4* vr, int phys, int u) {
     float mul_k = a.scale_log2;
     float mul_v = 1.f;
-    if constexpr (KV == PA_FP8_E4M3) {
-      mul_k *= a.k_scale[int64_t(phys) * H + head];
-      mul_v = a.v_scale[int64_t(phys) * H + head];
-    }
     const int jl = wave + (u / G::kSubs) * NW;  // block of the partition
     const int r0 = (blk0 + jl) * BS + (u % G::kSubs) * G::kSubRows;  // first token of the unit
     const int tok0 = r0 + grp;                    // token of load 0 in this lane's group
     const bool full = r0 + G::kSubRows <= L;
+    if constexpr (KV == PA_FP8_E4M3) {
+      if (kAppend && has_new && phys == new_blk) {
+        // the new row's block: its scales after the row (its earlier rows
+        // were requantised before the loop when a scale grew)
+        mul_k *= fk.s_new;
+        mul_v = fv.s_new;
+      } else {
+        mul_k *= a.k_scale[int64_t(phys) * H + head];
+        mul_v = a.v_scale[int64_t(phys) * H + head];
+      }
+    }
     if constexpr (kAppend) {
       if (has_new && r0 + G::kSubRows >= L) {   // the unit holding position L - 1
 #pragma unroll
@@ -411,6 +520,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
           ((new_slot / BS * H + head) * BS + new_slot % BS) * G::kRowBytes + lane * 16;
       *(uint4*)((char*)a.k_cache + dst) = knew;
       *(uint4*)((char*)a.v_cache + dst) = vnew;
+    }
+    if constexpr (KV == PA_FP8_E4M3) {
+      if (has_new && a.fp8_upkeep && lane == 0) {
+        // (the pool's scales are writable; the decode reads them through
+        // const pointers)
+        const_cast<float*>(a.k_scale)[new_blk * H + head] = fk.s_new;
+        const_cast<float*>(a.v_scale)[new_blk * H + head] = fv.s_new;
+      }
     }
   }
 
@@ -597,7 +714,7 @@ void launch_merge(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
 template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_t stream) {
   dim3 grid(a.num_heads, num_seqs, a.max_parts);
-  constexpr bool kCanAppend = KV != PA_FP8_E4M3;
+  constexpr bool kCanAppend = true;
   if (a.k_new && !kCanAppend) return hipErrorInvalidValue;
   if (a.k_new) {
     if constexpr (kCanAppend) {

@@ -73,6 +73,33 @@ __device__ __forceinline__ void store_from_f32(void* base, int64_t i, int dt, fl
     ((uint16_t*)base)[i] = f32_to_bf16_bits(x);
 }
 
+// ------------------------------------------------------- fp8 E4M3 storing
+
+// x / s rounded once in float32, then (pack4_fp8) RNE to E4M3FN saturating
+// at +-448.  Clamping first is exact: every |x/s| >= 448 rounds to 448 when
+// saturating.
+__device__ __forceinline__ float fp8_prep(float x, float s) {
+  const float y = __fdiv_rn(x, s);
+  return __builtin_isnan(y) ? y : fminf(fmaxf(y, -448.f), 448.f);
+}
+
+__device__ __forceinline__ uint32_t pack4_fp8(const float* y) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+  return (uint32_t)w;
+}
+
+// Eight codes requantised from scale s_old to divisor d:
+// RNE-saturate((decode(code) * s_old) / d), both steps rounded in float32.
+__device__ __forceinline__ uint2 requant8(uint2 w, float s_old, float d) {
+  float y[8];
+  const float2_t a0 = fp8x2_lo(w.x), a1 = fp8x2_hi(w.x), b0 = fp8x2_lo(w.y), b1 = fp8x2_hi(w.y);
+  const float x[8] = {a0.x, a0.y, a1.x, a1.y, b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fp8_prep(__fmul_rn(x[i], s_old), d);
+  return make_uint2(pack4_fp8(y), pack4_fp8(y + 4));
+}
+
 // -------------------------------------------------------------- reductions
 
 // DPP controls (GFX9 encoding).

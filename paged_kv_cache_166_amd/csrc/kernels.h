@@ -27,10 +27,14 @@ struct DecodeArgs {
   int32_t q_dtype;
   int32_t out_dtype;
   // pa_decode_append only (else NULL): the new row of each sequence,
-  // [num_seqs][num_heads][head_dim] of the KV type, and its slot (< 0: none)
+  // [num_seqs][num_heads][head_dim] of the KV type (fp8 pools: of q_dtype,
+  // quantised on the way in), and its slot (< 0: none)
   const void* k_new;
   const void* v_new;
   const int64_t* new_slots;
+  // fp8 pools with PA_POOL_FP8_AUTO_SCALE: the new rows keep each block's
+  // scale at amax / 448 (earlier rows requantised when it grows)
+  int32_t fp8_upkeep;
   // pa_decode_shared_prefix only (else 0): the first first_block blocks of
   // every table are the shared prefix, attended elsewhere into partitions
   // 0 .. prefix_parts-1; this launch covers the blocks after them, into

@@ -12,7 +12,8 @@ import torch
 
 import paged_kv_cache_166_amd as pa
 from oracle import cache as C
-from tests.gpu_util import TOL, Scenario, assert_close, bits_to_device, device_bits, to_bits
+from tests.gpu_util import (TOL, Scenario, assert_close, bits_to_device, device_bits, to_bits,
+                            values_f64)
 from tests.test_gpu_decode import _oracle
 
 pytestmark = pytest.mark.gpu
@@ -79,16 +80,73 @@ def test_append_equals_write_then_decode(kv, D, bs):
     sc.check_pool_bits()                     # the oracle's pool, rows written once
 
 
-def test_fp8_pools_are_refused():
-    sc = Scenario(8, 2, 16, 128, "fp8", seed=3)
-    sc.prompt(0, 5)
-    t_dev, ln_dev, _, _ = sc.device_tables([0])
-    q = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((1, 2, 128), dtype=torch.float32, device="cuda")
-    kn = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(NotImplementedError):
-        pa.pa_decode_append(out, q, sc.pool, kn, kn, torch.zeros(1, dtype=torch.int64, device="cuda"),
-                            t_dev, ln_dev, 0.1)
+@pytest.mark.parametrize("auto", [False, True])
+@pytest.mark.parametrize("qdt", ["bf16", "f16"])
+@pytest.mark.parametrize("D,bs", [(128, 32), (128, 16), (64, 4), (128, 64), (64, 64)])
+def test_fp8_append_equals_write_then_decode(auto, qdt, D, bs):
+    """fp8 pools: the new rows (of q's type) quantised by the decode launch --
+    with the blocks' scales kept up (PA_POOL_FP8_AUTO_SCALE: new rows whose
+    amplitude grows the block's amax requantise its earlier rows, rows that
+    start a block set a fresh scale) or with the caller's scales -- against
+    pa_reshape_and_cache of the same rows followed by pa_decode: outputs,
+    codes and scales bit for bit; then against the oracle at the fp8
+    tolerance."""
+    H = 3
+    lens = sorted({1, 2, bs, bs + 1, 2 * bs, 3 * bs - 1, 150, 600})   # lengths after the append
+    N = sum(-(-L // bs) for L in lens) + 5
+    sc = Scenario(N, H, bs, D, "fp8", seed=90 + D + bs, in_dtype=qdt,
+                  scale_range=(0.011, 0.03), fp8_auto_scale=auto)
+    rng = np.random.default_rng(D + bs + auto)
+    for i, L in enumerate(lens):
+        sc.prompt(i, L - 1, amp=rng.uniform(0.2, 2.0, (max(L - 1, 1), H, 1))[:L - 1])
+    seqs = list(range(len(lens)))
+    slots = []
+    for i in seqs:
+        s_lib, cow = sc.alloc.append_tokens(i, 1)
+        s_ora, _ = sc.ora.append_tokens(i, 1)
+        assert list(s_lib) == s_ora and cow is None
+        slots += s_ora
+    slots[3] = -1                            # no new row for this one
+    amp = rng.choice([0.05, 1.0, 30.0], size=(len(seqs), H, 1)).astype(np.float32)
+    kb = to_bits(rng.standard_normal((len(seqs), H, D), dtype=np.float32) * amp, qdt)
+    vb = to_bits(rng.standard_normal((len(seqs), H, D), dtype=np.float32) * amp, qdt)
+    kn, vn = bits_to_device(kb, qdt, "cuda"), bits_to_device(vb, qdt, "cuda")
+    sl = torch.tensor(slots, dtype=torch.int64, device="cuda")
+    q_dev, q64 = sc.random_q(len(seqs), qdt)
+    t_dev, ln_dev, _, _ = sc.device_tables(seqs)
+    scale = 1 / math.sqrt(D)
+    p = sc.pool
+    base = [t.clone() for t in (p.k_cache, p.v_cache, p.k_scale, p.v_scale)]
+    # the oracle: the same rows written (with or without scale upkeep), then attention
+    w = C.write_rows_fp8_upkeep if auto else C.write_rows_fp8
+    kf = values_f64(kb, qdt).astype(np.float32)
+    vf = values_f64(vb, qdt).astype(np.float32)
+    w(sc.ok, kf, slots, sc.oks, bs)
+    w(sc.ov, vf, slots, sc.ovs, bs)
+    ref = _oracle(sc, seqs, q64, scale)
+    for pb in (0, 1, 3):
+        for t, b in zip((p.k_cache, p.v_cache, p.k_scale, p.v_scale), base):
+            t.copy_(b)
+        two = pa.PagedPool(p.k_cache.clone(), p.v_cache.clone(), p.k_scale.clone(),
+                           p.v_scale.clone(), kv_dtype=p.kv_dtype, fp8_auto_scale=auto)
+        pa.pa_reshape_and_cache(two, kn, vn, sl)
+        out2 = torch.empty((len(seqs), H, D), dtype=torch.float32, device="cuda")
+        pa.pa_decode(out2, q_dev, two, t_dev, ln_dev, scale, pb,
+                     pa.decode_workspace(two, len(seqs), t_dev.shape[1], pb))
+        out1 = torch.full((len(seqs), H, D), float("nan"), dtype=torch.float32, device="cuda")
+        pa.pa_decode_append(out1, q_dev, p, kn, vn, sl, t_dev, ln_dev, scale, pb,
+                            pa.decode_workspace(p, len(seqs), t_dev.shape[1], pb))
+        torch.cuda.synchronize()
+        what = f"fp8 auto={auto} q={qdt} D={D} bs={bs} pb={pb}"
+        assert np.array_equal(out1.cpu().numpy().view(np.uint32),
+                              out2.cpu().numpy().view(np.uint32)), what
+        for a_, b_ in ((p.k_cache, two.k_cache), (p.v_cache, two.v_cache),
+                       (p.k_scale, two.k_scale), (p.v_scale, two.v_scale)):
+            assert np.array_equal(device_bits(a_), device_bits(b_)), what
+        got = out1.cpu().numpy().astype(np.float64)
+        keep = [i for i in seqs if i != 3]     # seq 3 reads its unwritten (sentinel) last row
+        assert_close(got[keep], ref[keep], TOL["fp8"], what)
+    sc.check_pool_bits()                     # codes and scales against the oracle's
 
 
 def _append_step(sc, seqs, stream):
