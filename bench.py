@@ -1110,7 +1110,9 @@ def other_workloads(device, reps=20):
     torch.cuda.synchronize()
     kt, nb = d.kernel_stats()
     out["long_fp8_decode"] = {
-        "kernel": "pa_decode (decode_kernel + decode_merge_kernel), 256 partitions",
+        "kernel": ("pa_decode_append (the step's rows quantised with scale upkeep in the decode "
+                   "launch; decode_kernel + decode_merge_kernel), 256 partitions" if d.fused else
+                   "pa_decode (decode_kernel + decode_merge_kernel), 256 partitions"),
         "kernel_us": kt * 1e6, "kernel_us_spread": d.kernel_spread(), "bytes_per_launch": nb,
         "GBps": nb / kt / 1e9, "hbm_frac": nb / kt / 1e9 / HBM_PEAK_GBS,
         "config": d.workload_config()}
