@@ -4,9 +4,10 @@ A step is one pass of the whole path over one batch: the host allocator
 appends the step's tokens (one per sequence for decode, the chunk for
 prefill) and packs block tables, slots and lengths into one pinned buffer,
 which is copied to the device once; then, for every attention layer the step
-serves, copy-on-write block copies (if any), pa_reshape_and_cache of the
-step's new K/V rows into that layer's pool, and pa_decode (or
-pa_prefill_chunk) over it.  The default workload is a decode step of an
+serves, copy-on-write block copies (if any) and one decode launch that also
+stores the step's new K/V rows into that layer's pool (pa_decode_append;
+pa_decode_shared_prefix_append for the shared-prefix batch) -- or, for
+prefill, pa_reshape_and_cache of the chunk and pa_prefill_chunk.  The default workload is a decode step of an
 attention-only model with the LLaMA-13B shape (40 layers of 40 heads x 128,
 fp16 KV, 16-token blocks, 32 sequences of 128..2048 tokens); the block
 tables are shared by all layers, each layer has its own pool.  Pool contents,
@@ -153,8 +154,9 @@ class DecodeBench:
 
     A step serves `layers` attention layers: one host allocation and one
     upload of slots / tables / lengths (shared by every layer, as block tables
-    are), then, per layer, the cache write of the step's K/V into that
-    layer's pool and pa_decode over it."""
+    are), then, per layer, one decode launch over that layer's pool that also
+    stores the step's K/V rows (fused=False: pa_reshape_and_cache, then
+    pa_decode)."""
 
     def __init__(self, workload, steps, warmup, device, partition_blocks=None, layers=None,
                  stream_kv=None, fused=None):
@@ -243,6 +245,7 @@ class DecodeBench:
         self.scale = 1 / math.sqrt(self.D)
         self.ev = []
         self.step_bytes = []
+        self.step_unique = []
         self.cows = 0
 
     def _filled_pool(self, g):
@@ -312,6 +315,7 @@ class DecodeBench:
             self.ev.append(tm_all)
         if timed:
             self.step_bytes.append(self.decode_bytes(lens))
+            self.step_unique.append(self.unique_bytes(lens))
         self.last = (d, lens)
 
     def unique_bytes(self, lens):
@@ -713,6 +717,11 @@ class DecodeBench:
     def kernel_spread(self):
         return spread(self.launch_seconds())
 
+    def mean_unique_bytes(self):
+        """Mean distinct K/V bytes per launch over the timed steps (the
+        contexts grow by one token a step)."""
+        return float(np.mean(self.step_unique))
+
     def workload_config(self):
         c = self.cfg
         d = {"workload": self.name, "layers_per_step": self.layers, "batch": self.B,
@@ -1028,7 +1037,7 @@ def main():
         # the HBM has to deliver each distinct row once: with a shared prefix
         # (the same blocks in every table) the unique bytes are the basis,
         # the logical ones (the prefix counted per sequence) are reported apart
-        hbm_bytes = b.unique_bytes(b.last[1]) if args.workload == "prefix_cow" else kv_bytes
+        hbm_bytes = b.mean_unique_bytes() if args.workload == "prefix_cow" else kv_bytes
         ach = hbm_bytes / kt / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS,
@@ -1058,7 +1067,7 @@ def main():
         if args.workload == "long_fp8_decode":
             res["fp8_write"] = b.fp8_write_series()
         if args.workload == "prefix_cow":
-            ub = b.unique_bytes(b.last[1])
+            ub = b.mean_unique_bytes()
             res["unique_bytes_per_launch"] = ub
             res["unique_GBps"] = ub / kt / 1e9
             res["cow_copy"] = b.cow_copy_us()
@@ -1119,7 +1128,7 @@ def other_workloads(device, reps=20):
     del d
     torch.cuda.empty_cache()
     log("bench: other workloads: shared-prefix decode")
-    steps, warm = 8, 2
+    steps, warm = 30, 5
     d = DecodeBench("prefix_cow", steps, warm, device)
     for k in range(warm):
         d.step(k, False)
@@ -1127,7 +1136,7 @@ def other_workloads(device, reps=20):
         d.step(k, True)
     torch.cuda.synchronize()
     kt, logical = d.kernel_stats()
-    unique = d.unique_bytes(d.last[1])
+    unique = d.mean_unique_bytes()
     sp = d.shared_prefix_series(reps)
     # the workload's decode step as the bench runs it: the new rows stored
     # and the prefix read once (pa_decode_shared_prefix_append)

@@ -192,11 +192,6 @@ constexpr int kMaxPartBlocks = 256;
 
 constexpr int default_max_loads(int bs) { return bs >= 64 ? 4 : 8; }
 
-// Output element d of (seq, head) from the shared prefix's partials (max,
-// sum, unnormalised output of partitions 0 .. prefix_parts - 1, written by
-// the prefix pass that ran before this launch) and one more partial (M, S,
-// A): the log-sum-exp merge, M' = max(M, m_c), S' = S 2^(M - M') + l_c
-// 2^(m_c - M'), likewise A.
 // 16 codes requantised from scale s_old to divisor d (see requant8).
 __device__ __forceinline__ uint4 requant16(uint4 w, float s_old, float d) {
   const uint2 a = requant8(make_uint2(w.x, w.y), s_old, d);
@@ -255,6 +250,11 @@ __device__ __forceinline__ Fp8Row fp8_new_row(const void* src, int64_t off, int 
   return r;
 }
 
+// Output element d of (seq, head) from the shared prefix's partials (max,
+// sum, unnormalised output of partitions 0 .. prefix_parts - 1, written by
+// the prefix pass that ran before this launch) and one more partial (M, S,
+// A): the log-sum-exp merge, M' = max(M, m_c), S' = S 2^(M - M') + l_c
+// 2^(m_c - M'), likewise A.
 template <int D>
 __device__ __forceinline__ void merge_prefix_partials(const DecodeArgs& a, int seq, int head,
                                                       int d, float M, float S, float A) {
@@ -274,10 +274,10 @@ __device__ __forceinline__ void merge_prefix_partials(const DecodeArgs& a, int s
 }
 
 // One workgroup's work: (head, sequence, partition) = blockIdx (x, y, z).
-// kAppend (16-bit and fp32 pools): the step's new K/V row of each sequence
-// (position L - 1) comes with the call; the workgroup of the last partition
-// stores it at its slot and uses it from registers for that position, so no
-// wave reads the row while it is being written.
+// kAppend: the step's new K/V row of each sequence (position L - 1) comes
+// with the call; the workgroup of the last partition stores it at its slot
+// (fp8 pools: quantised there, see fp8_new_row) and uses it from registers
+// for that position, so no wave reads the row while it is being written.
 template <int KV, int D, int BS, int NW, bool kStreamV, int MaxL, bool kAppend = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G = Geo<KV, D, BS, MaxL>;

@@ -9,9 +9,11 @@
 // How: a workgroup of 4 wavefronts owns 128 query rows of one (sequence,
 // head); wave w owns 32 of them.  The keys are walked in tiles of 32 tokens
 // (one to eight blocks, found through the block table):
-//  * K and V tiles land in LDS as rows, by DMA (global_load_lds_dwordx4)
-//    into three-stage rings, two tiles in flight while one is consumed; one
-//    workgroup barrier per tile;
+//  * K and V tiles travel through registers into LDS rows: each wave loads
+//    its part of a tile with global_load_dwordx4 a tile ahead of the LDS
+//    ring, converts it in registers where needed and stores it with
+//    ds_write_b128 into a three-stage ring (the tile consumed, the next one,
+//    the one being filled); one workgroup barrier per tile;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16 (bf16 or fp16 inputs, fp32
 //    accumulate): A = K rows from LDS, B = the wave's Q rows, held in
 //    registers for the whole walk;
@@ -26,9 +28,8 @@
 //    operand is read from the V rows by gfx950's transposing LDS read
 //    (ds_read_b64_tr_b16) in the same permuted key order.  P is rounded to
 //    fp16 (bf16's 8 bits would cost up to ~5e-3 on rows of a few keys); for
-//    bf16 pools each wave converts the V chunks its own DMA brought in to
-//    fp16 in place, once the DMA has landed and before the barrier that
-//    publishes the tile;
+//    bf16 pools V is converted to fp16 in registers, between its load and
+//    its store into LDS;
 //  * tiles wholly above the causal diagonal are skipped per wave; only
 //    tiles that cross it are masked.
 // Workgroups are mapped so that all query tiles of one (sequence, head) run
@@ -91,8 +92,8 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 //
 // Issued as inline assembly with an immediate offset: the compiler's wait
 // insertion cannot tell the ring stages apart for this instruction and would
-// otherwise drain every DMA in flight before some of these reads.  The
-// caller waits with lds_wait_tr() before using the results.
+// otherwise wait for every memory operation in flight before some of these
+// reads.  The caller waits with lds_wait_tr() before using the results.
 template <int kOffset>
 __device__ __forceinline__ uint2 lds_read_tr16(uint32_t lds_addr) {
   static_assert(kOffset >= 0 && kOffset < 65536, "ds offset field");
@@ -171,7 +172,7 @@ constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 
 // Workgroup barrier without a memory fence: this wave's LDS accesses are
 // complete when it arrives, and the vector-memory waits before it are the
-// caller's (a fence would also wait for every DMA in flight); the empty asm
+// caller's (a fence would also wait for every global load in flight); the empty asm
 // keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
@@ -303,7 +304,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // The block table is read-only during the kernel: read it through the
   // constant address space so that the uniform lookups below are scalar
   // loads (a vector load here would make the wait for it also wait for every
-  // DMA issued before it).
+  // global load issued before it).
   // Entries are read as unsigned (block ids are never negative): widening
   // one to 64 bits is then free, and the compiler waits for a scalar load
   // only where the entry is used, not right after issuing it.
