@@ -714,17 +714,13 @@ void launch_merge(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
 template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_t stream) {
   dim3 grid(a.num_heads, num_seqs, a.max_parts);
-  constexpr bool kCanAppend = true;
-  if (a.k_new && !kCanAppend) return hipErrorInvalidValue;
   if (a.k_new) {
-    if constexpr (kCanAppend) {
-      if (stream_v)
-        hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, true>), grid,
-                           dim3(kWaves * 64), 0, stream, a);
-      else
-        hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, true>), grid,
-                           dim3(kWaves * 64), 0, stream, a);
-    }
+    if (stream_v)
+      hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, true>), grid, dim3(kWaves * 64),
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, true>), grid,
+                         dim3(kWaves * 64), 0, stream, a);
   } else if (stream_v) {
     hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, false>), grid, dim3(kWaves * 64),
                        0, stream, a);
