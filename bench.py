@@ -91,11 +91,25 @@ class Timer:
         return self.e0.elapsed_time(self.e1) * 1e-3
 
 
-def loop_seconds(call, n, warm=2):
+def warm_clocks(call, seconds=1.0):
+    """Back-to-back calls for about `seconds` before a timed series.  The GPU
+    lowers its clocks while it idles (the CPU baseline, host work between
+    series) and needs some hundreds of milliseconds of load to return to its
+    sustained clocks; a series of a few milliseconds right after an idle
+    period would time the ramp (up to 20% slower)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+
+
+def loop_seconds(call, n, warm=2, warm_s=1.0):
     """Mean duration of one call over n back-to-back calls on the current
     stream, bracketed by one event pair (no event between launches: an event
     record waits for the caches' write-back and would add its cost to every
-    launch it brackets)."""
+    launch it brackets), after warm_clocks(call, warm_s)."""
+    warm_clocks(call, warm_s)
     for _ in range(warm):
         call()
     tm = Timer()
@@ -690,6 +704,22 @@ class DecodeBench:
     def lens_now(self):
         return np.array([self.alloc.seq_len(int(i)) for i in self.ids], dtype=np.int64)
 
+    def warm(self, seconds=1.0):
+        """warm_clocks with the step's decode on the state the last step left
+        (no rows written, so the workload is unchanged)."""
+        if getattr(self, "last", None) is None:
+            return
+        d, _ = self.last
+        pool = self.pools[0]
+        if self.shared:
+            call = lambda: pa.pa_decode_shared_prefix(self.out, self.q[0], pool, d["tables"],
+                                                      d["lens"], self.shared, self.scale, self.pb,
+                                                      self.ws_sp)
+        else:
+            call = lambda: pa.pa_decode(self.out, self.q[0], pool, d["tables"], d["lens"],
+                                        self.scale, self.pb, self.ws)
+        warm_clocks(call, seconds)
+
     def decode_bytes(self, lens):
         """Algorithmic bytes of one pa_decode launch: every cached K and V row
         once, q, out, the table entries read and the lengths (and, for
@@ -877,7 +907,12 @@ class PrefillBench:
                 "TFLOPs": self.flops() / sec / 1e12,
                 "kv_bytes": 2 * H * D * sum(c + self.S for c in self.ctx)}
 
-    def loop_us(self, reps=20):
+    def warm(self, seconds=1.0):
+        """warm_clocks with the workload's launch (a batch allocated for it
+        and freed again, so the pool's state is unchanged)."""
+        self.loop_us(1, warm_s=seconds)
+
+    def loop_us(self, reps=20, warm_s=1.0):
         """The workload's launch (bf16 pool, the batch allocated once), mean
         of back-to-back calls under one event pair, in us."""
         ids = np.arange(self.next_id, self.next_id + self.B, dtype=np.int64)
@@ -887,7 +922,8 @@ class PrefillBench:
         t, ln = self.alloc.pack(ids, self.maxb)
         td, ld = torch.from_numpy(t).to(self.device), torch.from_numpy(ln).to(self.device)
         sec = loop_seconds(lambda: pa.pa_prefill_chunk(self.out, self.q, self.pool, td, ld,
-                                                       self.qsl, self.S, self.scale), reps)
+                                                       self.qsl, self.S, self.scale), reps,
+                           warm_s=warm_s)
         for sid in ids:
             self.alloc.free_seq(int(sid))
         return sec * 1e6
@@ -1000,6 +1036,7 @@ def main():
     torch.cuda.synchronize()
     for k in range(args.warmup):
         b.step(k, False)
+    b.warm()
     torch.cuda.synchronize()
     log("bench: warmup done")
     t0 = time.perf_counter()
@@ -1114,6 +1151,7 @@ def other_workloads(device, reps=20):
     d = DecodeBench("long_fp8_decode", steps, warm, device)
     for k in range(warm):
         d.step(k, False)
+    d.warm()
     for k in range(warm, warm + steps):
         d.step(k, True)
     torch.cuda.synchronize()
@@ -1132,6 +1170,7 @@ def other_workloads(device, reps=20):
     d = DecodeBench("prefix_cow", steps, warm, device)
     for k in range(warm):
         d.step(k, False)
+    d.warm()
     for k in range(warm, warm + steps):
         d.step(k, True)
     torch.cuda.synchronize()

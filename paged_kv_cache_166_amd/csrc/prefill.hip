@@ -449,14 +449,14 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
         uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float2_t lo = fp8x2_lo(src[j][i]), hi = fp8x2_hi(src[j][i]);
+          // two codes per conversion, exact (scale 1): every E4M3 value is
+          // a bf16 and an fp16 value
           if (QT == PA_BF16 && !raw_v[j]) {
-            // every E4M3 value is exact in bf16: its float32 bits, truncated
-            h[2 * i] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
-            h[2 * i + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+            h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[j][i], 1.0f, false));
+            h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[j][i], 1.0f, true));
           } else {
-            h[2 * i] = pack_f16(lo[0], lo[1]);
-            h[2 * i + 1] = pack_f16(hi[0], hi[1]);
+            h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[j][i], 1.0f, false));
+            h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[j][i], 1.0f, true));
           }
         }
         const int row = raw_row[j];
