@@ -69,7 +69,9 @@ struct Geo {
   static_assert(kLpr >= 4 && kLpr <= 32, "row must span 4..32 lanes");
 };
 
-template <int KV>
+// Per-lane arithmetic of one KV type; QT is the query's type where the
+// kernel is instantiated for it (fp8 pools with 16-bit queries), else KV.
+template <int KV, int QT = KV>
 struct KvOps;
 
 template <>
@@ -148,8 +150,44 @@ struct KvOps<PA_BF16> {
   }
 };
 
-template <>
-struct KvOps<PA_FP8_E4M3> {
+// fp8 codes against a 16-bit query kept in its own type: two codes per
+// exact conversion (v_cvt_scalef32_pk_{f16,bf16}_fp8, scale 1: every E4M3
+// value is an f16 and a bf16 value) into a v_dot2 with two query elements,
+// as the 16-bit pools do.
+template <int QT>
+struct Fp8Dot {
+  static constexpr int kEpl = 16;
+  struct Q { uint4 raw[2]; };  // 16 elements of QT
+  __device__ static Q load_q(const void* q, int64_t off, int) {
+    const uint4* p = (const uint4*)((const uint16_t*)q + off);
+    return Q{{p[0], p[1]}};
+  }
+  __device__ static float dot(const Q& q, uint4 k) {
+    const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+    const uint32_t qw[8] = {q.raw[0].x, q.raw[0].y, q.raw[0].z, q.raw[0].w,
+                            q.raw[1].x, q.raw[1].y, q.raw[1].z, q.raw[1].w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (QT == PA_BF16) {
+        const bf162_t k0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+        const bf162_t k1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[2 * i]), k0, s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[2 * i + 1]), k1, s,
+                                            false);
+      } else {
+        const half2_t k0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        const half2_t k1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
+        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[2 * i]), k0, s, false);
+        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[2 * i + 1]), k1, s, false);
+      }
+    }
+    return s;
+  }
+};
+
+template <int QT>
+struct KvOps<PA_FP8_E4M3, QT> {
   static constexpr int kEpl = 16;
   struct Q { float v[16]; };  // q converted to float32 once
   __device__ static Q load_q(const void* q, int64_t off, int q_dtype) {
@@ -185,6 +223,21 @@ struct KvOps<PA_FP8_E4M3> {
     }
   }
 };
+
+template <>
+struct KvOps<PA_FP8_E4M3, PA_BF16> : Fp8Dot<PA_BF16> {
+  __device__ static void axpy(float* acc, float p, uint4 v) {
+    KvOps<PA_FP8_E4M3, PA_FP8_E4M3>::axpy(acc, p, v);
+  }
+};
+
+template <>
+struct KvOps<PA_FP8_E4M3, PA_F16> : Fp8Dot<PA_F16> {
+  __device__ static void axpy(float* acc, float p, uint4 v) {
+    KvOps<PA_FP8_E4M3, PA_FP8_E4M3>::axpy(acc, p, v);
+  }
+};
+
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -278,10 +331,11 @@ __device__ __forceinline__ void merge_prefix_partials(const DecodeArgs& a, int s
 // with the call; the workgroup of the last partition stores it at its slot
 // (fp8 pools: quantised there, see fp8_new_row) and uses it from registers
 // for that position, so no wave reads the row while it is being written.
-template <int KV, int D, int BS, int NW, bool kStreamV, int MaxL, bool kAppend = false>
+template <int KV, int D, int BS, int NW, bool kStreamV, int MaxL, bool kAppend = false,
+          int QT = KV>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G = Geo<KV, D, BS, MaxL>;
-  using Ops = KvOps<KV>;
+  using Ops = KvOps<KV, QT>;
   constexpr int E = G::kEpl;
   static_assert(E == Ops::kEpl, "lane element count");
 
@@ -588,9 +642,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   }
 }
 
-template <int KV, int D, int BS, int NW, bool kStreamV, bool kAppend>
+template <int KV, int D, int BS, int NW, bool kStreamV, bool kAppend, int QT = KV>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  decode_body<KV, D, BS, NW, kStreamV, default_max_loads(BS), kAppend>(a);
+  decode_body<KV, D, BS, NW, kStreamV, default_max_loads(BS), kAppend, QT>(a);
 }
 
 // A batch over several pools (same heads, head_dim and KV type; e.g. the
@@ -711,22 +765,37 @@ void launch_merge(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
   }
 }
 
+template <int KV, int D, int BS, int QT>
+void launch_q(const DecodeArgs& a, bool stream_v, dim3 grid, hipStream_t stream) {
+  if (a.k_new) {
+    if (stream_v)
+      hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, true, QT>), grid,
+                         dim3(kWaves * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, true, QT>), grid,
+                         dim3(kWaves * 64), 0, stream, a);
+  } else if (stream_v) {
+    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, false, QT>), grid,
+                       dim3(kWaves * 64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, false, QT>), grid,
+                       dim3(kWaves * 64), 0, stream, a);
+  }
+}
+
 template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeArgs& a, bool stream_v, int num_seqs, hipStream_t stream) {
   dim3 grid(a.num_heads, num_seqs, a.max_parts);
-  if (a.k_new) {
-    if (stream_v)
-      hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, true>), grid, dim3(kWaves * 64),
-                         0, stream, a);
+  // fp8 pools: the body for the query's type (16-bit queries in v_dot2)
+  if constexpr (KV == PA_FP8_E4M3) {
+    if (a.q_dtype == PA_BF16)
+      launch_q<KV, D, BS, PA_BF16>(a, stream_v, grid, stream);
+    else if (a.q_dtype == PA_F16)
+      launch_q<KV, D, BS, PA_F16>(a, stream_v, grid, stream);
     else
-      hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, true>), grid,
-                         dim3(kWaves * 64), 0, stream, a);
-  } else if (stream_v) {
-    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, true, false>), grid, dim3(kWaves * 64),
-                       0, stream, a);
+      launch_q<KV, D, BS, KV>(a, stream_v, grid, stream);
   } else {
-    hipLaunchKernelGGL((decode_kernel<KV, D, BS, kWaves, false, false>), grid, dim3(kWaves * 64),
-                       0, stream, a);
+    launch_q<KV, D, BS, KV>(a, stream_v, grid, stream);
   }
   if ((a.max_parts > 1 || a.prefix_parts > 0) && !a.fuse_merge) launch_merge<D>(a, num_seqs, stream);
   return hipGetLastError();
