@@ -63,20 +63,23 @@ def test_tiny_decode_workload():
     assert a.num_free() == 1
 
 
-@pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "fp8", "fp8-f16q", "fp8-f32q"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("bs", [4, 8, 16, 32, 64])
 def test_decode_sweep(kv, D, bs):
     """Ragged lengths (0, 1, around the block size, several partitions) on a
-    shuffled pool whose unused bytes are NaN; automatic and forced split-K."""
+    shuffled pool whose unused bytes are NaN; automatic and forced split-K.
+    fp8 pools with each query type (bf16 and f16 queries take the kernel
+    instantiated for them, f32 queries the float path)."""
     H = 3
+    kv, qdt = {"fp8": ("fp8", "bf16"), "fp8-f16q": ("fp8", "f16"),
+               "fp8-f32q": ("fp8", "f32")}.get(kv, (kv, kv))
     lens = sorted({0, 1, max(bs - 1, 1), bs, bs + 1, 3 * bs + 2, 150, 301})
     N = sum(-(-L // bs) for L in lens) + 7
     sc = Scenario(N, H, bs, D, kv, seed=21 + D + bs, scale_range=(0.011, 0.03))
     for i, L in enumerate(lens):
         sc.prompt(i, L)
     seqs = list(range(len(lens)))
-    qdt = "bf16" if kv == "fp8" else kv
     q_dev, q64 = sc.random_q(len(seqs), qdt)
     scale = 1 / math.sqrt(D)
     ref = _oracle(sc, seqs, q64, scale)
