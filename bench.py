@@ -91,12 +91,12 @@ class Timer:
         return self.e0.elapsed_time(self.e1) * 1e-3
 
 
-def warm_clocks(call, seconds=1.0):
+def warm_clocks(call, seconds=2.0):
     """Back-to-back calls for about `seconds` before a timed series.  The GPU
     lowers its clocks while it idles (the CPU baseline, host work between
-    series) and needs some hundreds of milliseconds of load to return to its
-    sustained clocks; a series of a few milliseconds right after an idle
-    period would time the ramp (up to 20% slower)."""
+    series) and needs a second or more of load to return to its sustained
+    clocks; a series of a few milliseconds right after an idle period would
+    time the ramp (up to 20% slower)."""
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(8):
@@ -104,7 +104,7 @@ def warm_clocks(call, seconds=1.0):
         torch.cuda.synchronize()
 
 
-def loop_seconds(call, n, warm=2, warm_s=1.0):
+def loop_seconds(call, n, warm=2, warm_s=2.0):
     """Mean duration of one call over n back-to-back calls on the current
     stream, bracketed by one event pair (no event between launches: an event
     record waits for the caches' write-back and would add its cost to every
@@ -708,7 +708,7 @@ class DecodeBench:
     def lens_now(self):
         return np.array([self.alloc.seq_len(int(i)) for i in self.ids], dtype=np.int64)
 
-    def warm(self, seconds=1.0):
+    def warm(self, seconds=2.0):
         """warm_clocks with the step's decode on the state the last step left
         (no rows written, so the workload is unchanged)."""
         if getattr(self, "last", None) is None:
@@ -911,12 +911,12 @@ class PrefillBench:
                 "TFLOPs": self.flops() / sec / 1e12,
                 "kv_bytes": 2 * H * D * sum(c + self.S for c in self.ctx)}
 
-    def warm(self, seconds=1.0):
+    def warm(self, seconds=2.0):
         """warm_clocks with the workload's launch (a batch allocated for it
         and freed again, so the pool's state is unchanged)."""
         self.loop_us(1, warm_s=seconds)
 
-    def loop_us(self, reps=20, warm_s=1.0):
+    def loop_us(self, reps=20, warm_s=2.0):
         """The workload's launch (bf16 pool, the batch allocated once), mean
         of back-to-back calls under one event pair, in us."""
         ids = np.arange(self.next_id, self.next_id + self.B, dtype=np.int64)

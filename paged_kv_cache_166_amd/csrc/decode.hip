@@ -40,6 +40,8 @@
 //    fences per workgroup; on this chip they write back and invalidate the
 //    whole L2 and cost far more than a second launch.)
 // Scores live in the log2 domain: s = log2(e) * scale * q.k, p = exp2(s - m).
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 // kMaxGroups entries), then runs the body of its group's block size with
 // sub-tiles of at most 4 wave-loads, so that every branch fits the same
 // register budget.  Partitions are part_tokens long in every group.
-template <int KV, int D, int NW, bool kStreamV>
+template <int KV, int D, int NW, bool kStreamV, int QT = KV>
 __global__ __launch_bounds__(NW * 64) void decode_multi_kernel(DecodeMultiArgs m) {
   const int seq = blockIdx.y;
   int g = 0;
@@ -672,11 +674,11 @@ __global__ __launch_bounds__(NW * 64) void decode_multi_kernel(DecodeMultiArgs m
   a.block_size = grp.block_size;
   a.part_blocks = m.part_tokens / grp.block_size;
   switch (grp.block_size) {
-    case 4: decode_body<KV, D, 4, NW, kStreamV, 4>(a); break;
-    case 8: decode_body<KV, D, 8, NW, kStreamV, 4>(a); break;
-    case 16: decode_body<KV, D, 16, NW, kStreamV, 4>(a); break;
-    case 32: decode_body<KV, D, 32, NW, kStreamV, 4>(a); break;
-    case 64: decode_body<KV, D, 64, NW, kStreamV, 4>(a); break;
+    case 4: decode_body<KV, D, 4, NW, kStreamV, 4, false, QT>(a); break;
+    case 8: decode_body<KV, D, 8, NW, kStreamV, 4, false, QT>(a); break;
+    case 16: decode_body<KV, D, 16, NW, kStreamV, 4, false, QT>(a); break;
+    case 32: decode_body<KV, D, 32, NW, kStreamV, 4, false, QT>(a); break;
+    case 64: decode_body<KV, D, 64, NW, kStreamV, 4, false, QT>(a); break;
   }
 }
 
@@ -825,12 +827,27 @@ template <int KV, int D>
 hipError_t launch_multi_t(const DecodeMultiArgs& m, bool stream_v, int num_seqs,
                           hipStream_t stream) {
   dim3 grid(m.base.num_heads, num_seqs, m.base.max_parts);
-  if (stream_v)
-    hipLaunchKernelGGL((decode_multi_kernel<KV, D, kWaves, true>), grid, dim3(kWaves * 64), 0,
-                       stream, m);
-  else
-    hipLaunchKernelGGL((decode_multi_kernel<KV, D, kWaves, false>), grid, dim3(kWaves * 64), 0,
-                       stream, m);
+  // fp8 pools: the body for the query's type, as launch_t picks it (the
+  // same arithmetic as pa_decode, bit for bit)
+  auto go = [&](auto qt_c) {
+    constexpr int QT = decltype(qt_c)::value;
+    if (stream_v)
+      hipLaunchKernelGGL((decode_multi_kernel<KV, D, kWaves, true, QT>), grid, dim3(kWaves * 64),
+                         0, stream, m);
+    else
+      hipLaunchKernelGGL((decode_multi_kernel<KV, D, kWaves, false, QT>), grid,
+                         dim3(kWaves * 64), 0, stream, m);
+  };
+  if constexpr (KV == PA_FP8_E4M3) {
+    if (m.base.q_dtype == PA_BF16)
+      go(std::integral_constant<int, PA_BF16>{});
+    else if (m.base.q_dtype == PA_F16)
+      go(std::integral_constant<int, PA_F16>{});
+    else
+      go(std::integral_constant<int, KV>{});
+  } else {
+    go(std::integral_constant<int, KV>{});
+  }
   if (m.base.max_parts > 1) {
     // The merge kernel counts a sequence's partitions as ceil(L / block_size
     // / part_blocks): in tokens, with block_size 1.

@@ -669,25 +669,55 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       // the same key order as P; two dimension blocks' operands per wait.
       const uint32_t vbase =
           uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)vl));
-      auto pv_step = [&](auto tt_c) {
-        constexpr int tt = decltype(tt_c)::value;
+      // Groups g = (tt, pair of dimension blocks) of four transposing
+      // reads; group g + 1's reads are in flight while group g's MFMAs
+      // issue (LDS operations complete in order: at most four outstanding
+      // means group g has landed).
+      constexpr int kGroups = 2 * (kDBlocks / 2);
+      auto read_grp = [&](auto g_c, uint2 (&v)[4]) {
+        constexpr int g = decltype(g_c)::value;
+        constexpr int tt = g / (kDBlocks / 2);
+        constexpr int db0 = 2 * (g % (kDBlocks / 2));
+        v[0] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0) << 6));
+        v[1] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0) << 6));
+        v[2] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0 + 1) << 6));
+        v[3] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0 + 1) << 6));
+      };
+      auto mfma_grp = [&](auto g_c, const uint2 (&v)[4]) {
+        constexpr int g = decltype(g_c)::value;
+        constexpr int tt = g / (kDBlocks / 2);
+        constexpr int db0 = 2 * (g % (kDBlocks / 2));
 #pragma unroll
-        for (int db0 = 0; db0 < kDBlocks; db0 += 2) {
-          uint2 v[4];
-          v[0] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0) << 6));
-          v[1] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0) << 6));
-          v[2] = lds_read_tr16<(16 * tt) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0 + 1) << 6));
-          v[3] = lds_read_tr16<(16 * tt + 8) * kRowBytes>(vbase + xor_here(vt_lane, uint32_t(db0 + 1) << 6));
-          lds_wait_tr(v);
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const uint4 va = make_uint4(v[2 * k].x, v[2 * k].y, v[2 * k + 1].x, v[2 * k + 1].y);
-            o[db0 + k] = mfma_pv(va, pf[tt], o[db0 + k]);
-          }
+        for (int k = 0; k < 2; ++k) {
+          const uint4 va = make_uint4(v[2 * k].x, v[2 * k].y, v[2 * k + 1].x, v[2 * k + 1].y);
+          o[db0 + k] = mfma_pv(va, pf[tt], o[db0 + k]);
         }
       };
-      pv_step(std::integral_constant<int, 0>{});
-      pv_step(std::integral_constant<int, 1>{});
+      auto wait4 = [](uint2 (&v)[4]) {
+        asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+      };
+      using G0 = std::integral_constant<int, 0>;
+      using G1 = std::integral_constant<int, 1>;
+      uint2 va[4], vb[4];
+      read_grp(G0{}, va);
+      read_grp(G1{}, vb);
+      wait4(va);
+      mfma_grp(G0{}, va);
+      if constexpr (kGroups == 4) {
+        using G2 = std::integral_constant<int, 2>;
+        using G3 = std::integral_constant<int, 3>;
+        read_grp(G2{}, va);
+        wait4(vb);
+        mfma_grp(G1{}, vb);
+        read_grp(G3{}, vb);
+        wait4(va);
+        mfma_grp(G2{}, va);
+        lds_wait_tr(vb);
+        mfma_grp(G3{}, vb);
+      } else {
+        lds_wait_tr(vb);
+        mfma_grp(G1{}, vb);
+      }
     }
     wg_barrier();
   };
