@@ -83,7 +83,9 @@ WsLayout ws_layout_parts(const pa_pool* p, int32_t num_seqs, int32_t parts) {
 }
 
 // The shared-prefix decode's geometry: prefix chunks (whole 32-key tiles,
-// at least 128 keys, at most about 64 chunks) and suffix partitions.
+// at least 256 keys, at most about 64 chunks) and suffix partitions.  A
+// chunk's workgroup costs about the same from 4 to 8 tiles (its fixed
+// latency dominates), while each chunk adds a partial per (sequence, head).
 struct PrefixPlan {
   int32_t prefix_len, chunk_keys, chunks, suffix_pb, suffix_parts, total_parts;
 };
@@ -93,7 +95,7 @@ PrefixPlan prefix_plan(const pa_pool* p, int32_t max_blocks, int32_t shared_bloc
   PrefixPlan g{};
   g.prefix_len = shared_blocks * p->block_size;
   const int32_t want = int32_t((int64_t(g.prefix_len) + 63) / 64);
-  g.chunk_keys = std::max<int32_t>(128, (want + 31) / 32 * 32);
+  g.chunk_keys = std::max<int32_t>(256, (want + 31) / 32 * 32);
   g.chunks = (g.prefix_len + g.chunk_keys - 1) / g.chunk_keys;
   g.suffix_pb = partition_blocks > 0 ? partition_blocks : auto_partition_blocks(p);
   g.suffix_parts = (max_blocks - shared_blocks + g.suffix_pb - 1) / g.suffix_pb;

@@ -61,12 +61,13 @@ def test_sweep(kv, D, bs):
 
 
 def test_long_prefix_takes_wider_chunks():
-    """A 9600-token prefix (more than 64 chunks of 128 keys)."""
-    sc = _batch("bf16", 128, 64, 2, 150, [0, 9, 130, 64], seed=9)
+    """A 20480-token prefix (more than 64 chunks of 256 keys, so the chunks
+    widen to 320 keys)."""
+    sc = _batch("bf16", 128, 64, 2, 320, [0, 9, 130, 64], seed=9)
     seqs = [0, 1, 2, 3]
     q_dev, q64 = sc.random_q(4, "bf16")
     ref = _oracle(sc, seqs, q64, 0.1)
-    assert_close(_run(sc, seqs, q_dev, 150, 0.1), ref, TOL["bf16"], "long prefix")
+    assert_close(_run(sc, seqs, q_dev, 320, 0.1), ref, TOL["bf16"], "long prefix")
 
 
 def test_prefix_cow_workload():
