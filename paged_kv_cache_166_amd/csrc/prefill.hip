@@ -33,8 +33,12 @@
 //  * tiles wholly above the causal diagonal are skipped per wave; only
 //    tiles that cross it are masked.
 // Workgroups are mapped so that all query tiles of one (sequence, head) run
-// on the same XCD (its L2 holds that head's K/V); the last query tile, which
-// sees the most keys, is dispatched first.
+// on the same XCD (its L2 holds that head's K/V).  In batches of up to 64
+// (sequence, query tile) classes each XCD takes its work items longest
+// first (a longest-processing-time order over the classes' key-tile
+// counts, which each workgroup ranks in its prologue), so the short items
+// fill the end of the launch; larger batches go pair by pair, the last query
+// tile of a pair (it sees the most keys) first.
 #include <type_traits>
 
 #include "device.h"
@@ -52,6 +56,24 @@ constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBM = kWaves * kQW;       // query rows per workgroup
 constexpr int kBN = 32;                 // keys per tile
 constexpr int kXcds = 8;
+// Longest work first: batches of at most this many (sequence, query tile)
+// classes have their workgroups dispatched in order of decreasing key-tile
+// count (each workgroup ranks the classes in its prologue).
+constexpr int kMaxLptClasses = 64;
+
+__host__ __device__ inline bool lpt_order(int num_seqs, int num_qtiles) {
+  return num_seqs * num_qtiles <= kMaxLptClasses;
+}
+
+// Heads h in [0, H) whose pair seq * H + h is dealt to XCD x (pair % 8 == x):
+// the first one and how many.
+__device__ __forceinline__ int first_head_on(int x, int seq, int H) {
+  return ((x - seq * H) % kXcds + kXcds) % kXcds;
+}
+__device__ __forceinline__ int heads_on(int x, int seq, int H) {
+  const int h0 = first_head_on(x, seq, H);
+  return h0 < H ? (H - 1 - h0) / kXcds + 1 : 0;
+}
 
 template <int KV>
 __device__ __forceinline__ f32x16_t mfma_qk(uint4 a, uint4 b, f32x16_t c) {
@@ -255,15 +277,65 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   auto swz_v = [](int r) { return 4 * ((r * kChunks / 16) % (kChunks / 4)); };
 
   // Work item: (pair = seq * H + head, query tile); pairs are dealt to XCDs
-  // round robin by pair, the query tiles of a pair go to the same XCD, last
-  // tile first.
+  // round robin by pair (pair % 8), so all query tiles of a pair share an
+  // XCD and its L2.  In a batch of few (sequence, query tile) classes, each
+  // XCD takes its items in order of decreasing work (classes ranked by key
+  // tiles, ties by class index; heads in order within a class), so the
+  // longest items start first and the short ones fill the end of the launch.
+  // Otherwise pairs go in order, the query tiles of a pair last tile first.
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
   const int g = lin / kXcds;
-  const int pair = xcd + kXcds * (g / num_qtiles);
-  if (pair >= num_pairs) return;
-  const int qtile = num_qtiles - 1 - (g % num_qtiles);
   const int H = a.num_heads;
+  int pair, qtile;
+  if (!kPrefix && lpt_order(a.num_seqs, num_qtiles)) {
+    int* cost = (int*)lds_v2;          // [n] key tiles of class u (0: no rows)
+    int* order = cost + kMaxLptClasses;  // [n] class at sorted position r
+    int* sel = order + kMaxLptClasses;   // this workgroup's class and index in it
+    const int n = a.num_seqs * num_qtiles;
+    const int tid = threadIdx.x;
+    if (tid == 0) sel[0] = -1;
+    if (tid < n) {
+      const int sq = tid / num_qtiles, qt = num_qtiles - 1 - tid % num_qtiles;
+      const int q0 = a.query_start_loc[sq];
+      const int Sq = a.query_start_loc[sq + 1] - q0;
+      const int keys = a.context_lens[sq] - Sq + min((qt + 1) * kBM, Sq);
+      cost[tid] = qt * kBM < Sq ? (keys + kBN - 1) / kBN : 0;
+    }
+    __syncthreads();
+    if (tid < n) {
+      const int c = cost[tid];
+      int r = 0;
+      for (int u = 0; u < n; ++u) {
+        const int cu = cost[u];
+        r += (cu > c) || (cu == c && u < tid);
+      }
+      order[r] = tid;
+    }
+    __syncthreads();
+    if (tid < n) {
+      // items on this XCD before sorted position tid, and at it
+      int before = 0;
+      for (int r = 0; r < tid; ++r) before += heads_on(xcd, order[r] / num_qtiles, H);
+      const int here = heads_on(xcd, order[tid] / num_qtiles, H);
+      if (g >= before && g < before + here) {
+        sel[0] = order[tid];
+        sel[1] = g - before;
+      }
+    }
+    __syncthreads();
+    const int c = sel[0];
+    const int j = sel[1];
+    __syncthreads();  // the scratch is LDS the ring uses later
+    if (c < 0) return;
+    const int sq = c / num_qtiles;
+    qtile = num_qtiles - 1 - c % num_qtiles;
+    pair = sq * H + first_head_on(xcd, sq, H) + kXcds * j;
+  } else {
+    pair = xcd + kXcds * (g / num_qtiles);
+    if (pair >= num_pairs) return;
+    qtile = num_qtiles - 1 - (g % num_qtiles);
+  }
   const int head = pair % H;
   // kPrefix: pair = (chunk, head); keys [k0, L) of the prefix
   const int chunk = kPrefix ? pair / H : 0;
@@ -768,7 +840,11 @@ hipError_t launch_t(const PrefillArgs& a, int max_query_len, hipStream_t stream)
   const int num_qtiles = (max_query_len + kBM - 1) / kBM;
   const int num_pairs = a.num_seqs * a.num_heads;
   const int padded_pairs = (num_pairs + kXcds - 1) / kXcds * kXcds;
-  const int64_t blocks = int64_t(padded_pairs) * num_qtiles;
+  // longest-first order: at most ceil(H / 8) items of each class per XCD
+  const int64_t blocks =
+      lpt_order(a.num_seqs, num_qtiles)
+          ? int64_t(kXcds) * a.num_seqs * num_qtiles * ((a.num_heads + kXcds - 1) / kXcds)
+          : int64_t(padded_pairs) * num_qtiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_kernel<KV, QT, D, BS>), dim3(unsigned(blocks)), dim3(kWaves * 64), 0,
                      stream, a, num_qtiles, num_pairs);

@@ -54,6 +54,27 @@ def test_prefill_sweep(kv, D, bs):
     assert np.all(np.abs(got - ref) <= TOL[kv] + half_ulp(kv, ref)), "low-precision output"
 
 
+@pytest.mark.parametrize("nseq", [16, 24])
+def test_prefill_dispatch_orders(nseq):
+    """Both work orders of the launch: 16 sequences x 3 query tiles (48
+    classes: longest work first, each workgroup ranking the classes) and 24
+    (72 classes: pairs in order), 5 heads (an uneven number of heads per XCD),
+    ragged contexts and chunks from 1 to 300 rows, some classes without rows."""
+    rng = np.random.default_rng(61 + nseq)
+    ctx = [int(c) for c in rng.integers(0, 400, nseq)]
+    chunk = [int(c) for c in rng.integers(1, 301, nseq)]
+    chunk[0] = 300                      # three query tiles
+    bs = 16
+    N = sum(-(-(c + s) // bs) for c, s in zip(ctx, chunk)) + 8
+    sc = Scenario(N, 5, bs, 64, "bf16", seed=63 + nseq)
+    seqs, qsl, q_dev, q64 = _setup(sc, ctx, chunk, "bf16")
+    scale = 1 / math.sqrt(64)
+    tables, lens = sc.oracle_tables(seqs)
+    ref = A.prefill_chunk(q64, qsl, sc.ok, sc.ov, "bf16", tables, lens, bs, scale)
+    got = _run(sc, seqs, qsl, q_dev, scale)
+    assert_close(got, ref, TOL["bf16"], f"dispatch order, {nseq} sequences")
+
+
 def test_prefill_whole_sequence_is_causal_attention():
     """No earlier context: the chunk is the whole sequence (top-left mask)."""
     sc = Scenario(12, 3, 32, 128, "bf16", seed=45)
