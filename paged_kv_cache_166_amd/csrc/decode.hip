@@ -750,14 +750,65 @@ __global__ __launch_bounds__(DC * R) void decode_merge_kernel(DecodeArgs a) {
   store_from_f32(a.out, sh * D + d, a.out_dtype, Sg > 0.f ? Ag / Sg : 0.f);
 }
 
+// The merge for workspaces of at most P partitions per sequence: one thread
+// per output element, with every partition's triple loaded before the
+// context length is known (one round trip to memory).  Same operations, in
+// the same order, as decode_merge_kernel<D, R, D> for sequences of at most
+// R partitions.
+template <int D, int P>
+__global__ __launch_bounds__(D) void decode_merge_small_kernel(DecodeArgs a) {
+  const int head = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int H = a.num_heads;
+  const int d = threadIdx.x;
+  const int64_t sh = int64_t(seq) * H + head;
+  const float* ml = a.ws_ml + 2 * sh * a.ws_parts;
+  const float* pa = a.ws_acc + sh * a.ws_parts * D + d;
+  float m[P], l[P], x[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    m[p] = kNoMax;
+    l[p] = 0.f;
+    x[p] = 0.f;
+    if (p < a.ws_parts) {
+      m[p] = ml[2 * p];
+      l[p] = ml[2 * p + 1];
+      x[p] = pa[int64_t(p) * D];
+    }
+  }
+  const int L = a.context_lens[seq];
+  const int nblocks = (L + a.block_size - 1) / a.block_size;
+  const int nparts = a.prefix_parts + (nblocks > a.first_block
+                                           ? (nblocks - a.first_block + a.part_blocks - 1) /
+                                                 a.part_blocks
+                                           : 0);
+  if (nparts <= 1 && a.prefix_parts == 0) return;
+  float M = kNoMax;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p < nparts) M = fmaxf(M, m[p]);
+  float A = 0.f, S = 0.f;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p < nparts) {
+      const float f = fast_exp2(m[p] - M);
+      A = fmaf(x[p], f, A);
+      S = fmaf(l[p], f, S);
+    }
+  store_from_f32(a.out, sh * D + d, a.out_dtype, S > 0.f ? A / S : 0.f);
+}
+
 constexpr int kWaves = 4;
 
-// The merge launch: up to 16 partitions, 512 / D threads per element over
-// all D elements in one workgroup; more, 16 threads per element over 64
-// elements per workgroup.
+// The merge launch: up to 8 partitions, one thread per element; up to 16,
+// 512 / D threads per element over all D elements in one workgroup; more,
+// 16 threads per element over 64 elements per workgroup.
 template <int D>
 void launch_merge(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
-  if (a.ws_parts <= 16) {
+  if (a.ws_parts <= 8) {
+    hipLaunchKernelGGL((decode_merge_small_kernel<D, 8>), dim3(a.num_heads, num_seqs), dim3(D), 0,
+                       stream, a);
+  } else if (a.ws_parts <= 16) {
     constexpr int R = 512 / D;
     hipLaunchKernelGGL((decode_merge_kernel<D, R, D>), dim3(a.num_heads, num_seqs), dim3(D * R),
                        0, stream, a);
