@@ -770,6 +770,14 @@ class DecodeBench:
         d["fp8_auto_scale"] = self.auto_scale
         return d
 
+    def merge_kernel(self):
+        """The merge launch behind a split decode: one thread per output
+        element when the workspace holds at most 8 partitions per (sequence,
+        head), the strided LDS merge beyond that."""
+        pb = self.pb or pa.pa_decode_auto_partition_blocks(self.pool, self.B, self.maxb)
+        parts = -(-self.maxb // pb)
+        return "decode_merge_small_kernel" if parts <= 8 else "decode_merge_kernel"
+
     def cpu_baseline(self, budget_s=10.0):
         """The oracle on the same shape: (sequence, head) decodes of the batch
         at the prompt lengths (pool rows filled by torch before any library
@@ -1087,7 +1095,7 @@ def main():
                                       "pass + decode_kernel with the merge fused)"
                                       if getattr(b, "shared", 0) else
                                       ("pa_decode_append" if b.fused else "pa_decode")
-                                      + " (decode_kernel + decode_merge_kernel)"),
+                                      + f" (decode_kernel + {b.merge_kernel()})"),
                            "kernel_us": kt * 1e6, "kernel_us_spread": b.kernel_spread(),
                            "bytes_per_launch": hbm_bytes,
                            "basis": "unique bytes" if args.workload == "prefix_cow"
@@ -1162,8 +1170,8 @@ def other_workloads(device, reps=20):
     kt, nb = d.kernel_stats()
     out["long_fp8_decode"] = {
         "kernel": ("pa_decode_append (the step's rows quantised with scale upkeep in the decode "
-                   "launch; decode_kernel + decode_merge_kernel), 256 partitions" if d.fused else
-                   "pa_decode (decode_kernel + decode_merge_kernel), 256 partitions"),
+                   f"launch; decode_kernel + {d.merge_kernel()}), 256 partitions" if d.fused else
+                   f"pa_decode (decode_kernel + {d.merge_kernel()}), 256 partitions"),
         "kernel_us": kt * 1e6, "kernel_us_spread": d.kernel_spread(), "bytes_per_launch": nb,
         "GBps": nb / kt / 1e9, "hbm_frac": nb / kt / 1e9 / HBM_PEAK_GBS,
         "config": d.workload_config()}
