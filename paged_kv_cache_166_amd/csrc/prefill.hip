@@ -56,6 +56,8 @@ constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBM = kWaves * kQW;       // query rows per workgroup
 constexpr int kBN = 32;                 // keys per tile
 constexpr int kXcds = 8;
+// Buffer resource flags (dword 3) for plain 32-bit raw buffer loads.
+constexpr int kBufferFlags = 0x00020000;
 // Longest work first: batches of at most this many (sequence, query tile)
 // classes have their workgroups dispatched in order of decreasing key-tile
 // count (each workgroup ranks the classes in its prologue).
@@ -352,6 +354,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < kWaves);  // (fp8 pools: which raw loads are V)
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -445,8 +448,43 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // Loads of this wave's part of tile t into the staging registers.
   // blk_hint: wave_blk(t) where kOneBlockPerWave.
   u32x4_t stg[kStage];
+  // fp8 pools whose blocks hold whole tiles: a tile's K and V scales are
+  // vector loads issued with its codes (in order with them, so no scalar
+  // read waits inside the Q K^T chain), moved to scalar registers of the
+  // tile's stage when the codes are stored.
+  constexpr bool kScaleStaged = kFp8 && BS >= kBN;
+  const __amdgpu_buffer_rsrc_t ksc_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.k_scale, 0, 0x7fffffff, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vsc_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.v_scale, 0, 0x7fffffff, kBufferFlags);
+  uint32_t stg_sc[2];
+  float sc0[2], sc1[2], sc2[2];
+  auto stage_sc = [&](auto st) -> float (&)[2] {
+    if constexpr (decltype(st)::value == 0) return sc0;
+    else if constexpr (decltype(st)::value == 1) return sc1;
+    else return sc2;
+  };
   auto load_tile = [&](u32x4_t (&dst)[kStage], int t, uint32_t blk_hint) {
     const int kb = (t0 + t) * kBN;
+    if constexpr (kFp8 && BS >= kBN) {
+      // The tile lies in one block (tiles start at multiples of kBN, blocks
+      // are multiples of it) and starts before L, so its block is the table
+      // entry of kb, which holds L - 1 whenever the tile reaches past it:
+      // a uniform base, and keys past the end re-read the last key (finite
+      // data; those keys are masked).
+      const uint32_t blk = table[__builtin_amdgcn_readfirstlane(int(unsigned(kb) / BS))];
+      const int64_t base = int64_t(blk) * blk_stride + head_off;
+      const int32_t sc_off = int32_t((int64_t(blk) * H + head) * 4);
+      stg_sc[0] = __builtin_amdgcn_raw_buffer_load_b32(ksc_rsrc, 0, sc_off, 0);
+      stg_sc[1] = __builtin_amdgcn_raw_buffer_load_b32(vsc_rsrc, 0, sc_off, 0);
+#pragma unroll
+      for (int j = 0; j < kRawLoadsPerWave; ++j) {
+        const int keyc = min(kb + raw_row[j], L - 1);
+        const uint32_t off = uint32_t(unsigned(keyc) % BS) * D + raw_piece * 16;
+        dst[j] = *(const u32x4_t*)((const char*)(raw_v[j] ? a.v_cache : a.k_cache) + base + off);
+      }
+      return;
+    }
     if constexpr (kFp8) {
       // Per-lane addresses over at most kRawBlocksPerLoad blocks (scalar
       // table reads); keys past the end re-read the last key (finite data;
@@ -536,6 +574,11 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
         const int sw = raw_v[j] ? swz_v(row) : swz_k(row);
         *(u32x4_t*)(dst + ((2 * raw_piece) ^ sw) * 16) = u32x4_t{h[0], h[1], h[2], h[3]};
         *(u32x4_t*)(dst + ((2 * raw_piece + 1) ^ sw) * 16) = u32x4_t{h[4], h[5], h[6], h[7]};
+      }
+      if constexpr (kScaleStaged) {
+        float (&d)[2] = stage_sc(st);
+        d[0] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(stg_sc[0]));
+        d[1] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(stg_sc[1]));
       }
     } else {
 #pragma unroll
@@ -635,7 +678,10 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       // fp8 pools: the K and V scales of the tile's blocks (scalar reads,
       // issued before the MFMAs that they wait behind).
       float sk[kScaleBlocks], sv[kScaleBlocks];
-      if constexpr (kFp8) {
+      if constexpr (kScaleStaged) {
+        sk[0] = stage_sc(st)[0];
+        sv[0] = stage_sc(st)[1];
+      } else if constexpr (kFp8) {
 #pragma unroll
         for (int j = 0; j < kScaleBlocks; ++j) {
           const int64_t blk =
