@@ -230,7 +230,7 @@ __device__ __forceinline__ void wg_barrier() {
 template <int KV, int QT, int D, int BS, bool kPrefix = false>
 __global__ __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(((KV == PA_FP8_E4M3 && BS < 32) || (KV == PA_F16 && D == 128 && BS == 4)) ? 2 : 3)))
-void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
+void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq) {
   constexpr bool kFp8 = KV == PA_FP8_E4M3;
   constexpr int kRowBytes = D * 2;
   constexpr int kChunks = D / 8;                       // 16-byte chunks per row
@@ -281,9 +281,16 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   // Work item: (pair = seq * H + head, query tile); pairs are dealt to XCDs
   // round robin by pair (pair % 8), so all query tiles of a pair share an
   // XCD and its L2.  In a batch of few (sequence, query tile) classes, each
-  // XCD takes its items in order of decreasing work (classes ranked by key
-  // tiles, ties by class index; heads in order within a class), so the
-  // longest items start first and the short ones fill the end of the launch.
+  // XCD takes its items in order of decreasing work (heads in order within
+  // a class), so the longest items start first and the short ones fill the
+  // end of the launch:
+  // - lpt_by_seq = 0 (the grid is resident at once): classes ranked by key
+  //   tiles, ties by class index;
+  // - lpt_by_seq = 1 (several rounds of workgroups): classes ranked by the
+  //   largest key-tile count of their sequence, ties by class index, so a
+  //   sequence's query tiles stay together (last tile first) and the query
+  //   tiles of a head, which read the same K/V tiles, run side by side and
+  //   share them in the L2.
   // Otherwise pairs go in order, the query tiles of a pair last tile first.
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
@@ -294,6 +301,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
     int* cost = (int*)lds_v2;          // [n] key tiles of class u (0: no rows)
     int* order = cost + kMaxLptClasses;  // [n] class at sorted position r
     int* sel = order + kMaxLptClasses;   // this workgroup's class and index in it
+    int* scost = sel + 2;                // [n] largest key-tile count of u's sequence
+    static_assert((3 * kMaxLptClasses + 2) * sizeof(int) <= kTileBytes, "LPT scratch");
     const int n = a.num_seqs * num_qtiles;
     const int tid = threadIdx.x;
     if (tid == 0) sel[0] = -1;
@@ -305,11 +314,21 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
       cost[tid] = qt * kBM < Sq ? (keys + kBN - 1) / kBN : 0;
     }
     __syncthreads();
+    if (lpt_by_seq) {  // (uniform)
+      if (tid < n) {
+        const int s0 = (tid / num_qtiles) * num_qtiles;
+        int mc = 0;
+        for (int j = 0; j < num_qtiles; ++j) mc = max(mc, cost[s0 + j]);
+        scost[tid] = mc;
+      }
+      __syncthreads();
+    }
+    const int* key = lpt_by_seq ? scost : cost;
     if (tid < n) {
-      const int c = cost[tid];
+      const int c = key[tid];
       int r = 0;
       for (int u = 0; u < n; ++u) {
-        const int cu = cost[u];
+        const int cu = key[u];
         r += (cu > c) || (cu == c && u < tid);
       }
       order[r] = tid;
@@ -881,19 +900,41 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs) {
   }
 }
 
+// Workgroups of prefill_kernel<KV, QT, D, BS> resident on the GPU at once
+// (per CU by its registers and LDS, times the CUs), looked up once per
+// instantiation on the first launch's device; 0 if the runtime cannot say.
+template <int KV, int QT, int D, int BS>
+int64_t resident_workgroups() {
+  static const int64_t n = [] {
+    int dev = 0, per_cu = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel<KV, QT, D, BS>,
+                                                     kWaves * 64, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return int64_t(0);
+    return int64_t(per_cu) * cus;
+  }();
+  return n;
+}
+
 template <int KV, int QT, int D, int BS>
 hipError_t launch_t(const PrefillArgs& a, int max_query_len, hipStream_t stream) {
   const int num_qtiles = (max_query_len + kBM - 1) / kBM;
   const int num_pairs = a.num_seqs * a.num_heads;
   const int padded_pairs = (num_pairs + kXcds - 1) / kXcds * kXcds;
   // longest-first order: at most ceil(H / 8) items of each class per XCD
+  const bool lpt = lpt_order(a.num_seqs, num_qtiles);
   const int64_t blocks =
-      lpt_order(a.num_seqs, num_qtiles)
-          ? int64_t(kXcds) * a.num_seqs * num_qtiles * ((a.num_heads + kXcds - 1) / kXcds)
+      lpt ? int64_t(kXcds) * a.num_seqs * num_qtiles * ((a.num_heads + kXcds - 1) / kXcds)
           : int64_t(padded_pairs) * num_qtiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // Rank by sequence when the workgroups come in several rounds (a class
+  // ranking would then start a head's query tiles rounds apart and read its
+  // K/V several times); a grid resident at once keeps the class ranking,
+  // whose placement balances the work per CU.
+  const int by_seq = lpt && blocks > resident_workgroups<KV, QT, D, BS>() ? 1 : 0;
   hipLaunchKernelGGL((prefill_kernel<KV, QT, D, BS>), dim3(unsigned(blocks)), dim3(kWaves * 64), 0,
-                     stream, a, num_qtiles, num_pairs);
+                     stream, a, num_qtiles, num_pairs, by_seq);
   return hipGetLastError();
 }
 
@@ -918,7 +959,7 @@ hipError_t launch_prefix_t(const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = int64_t(padded_pairs) * num_qtiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_kernel<KV, QT, D, BS, true>), dim3(unsigned(blocks)),
-                     dim3(kWaves * 64), 0, stream, a, num_qtiles, num_pairs);
+                     dim3(kWaves * 64), 0, stream, a, num_qtiles, num_pairs, 0);
   return hipGetLastError();
 }
 
