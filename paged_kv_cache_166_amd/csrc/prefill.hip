@@ -467,18 +467,21 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
   // Loads of this wave's part of tile t into the staging registers.
   // blk_hint: wave_blk(t) where kOneBlockPerWave.
   u32x4_t stg[kStage];
-  // fp8 pools whose blocks hold whole tiles: a tile's K and V scales are
-  // vector loads issued with its codes (in order with them, so no scalar
-  // read waits inside the Q K^T chain), moved to scalar registers of the
-  // tile's stage when the codes are stored.
-  constexpr bool kScaleStaged = kFp8 && BS >= kBN;
+  // fp8 pools: a tile's K and V scales, one pair per block, are vector
+  // loads issued with its codes (in order with them, so no scalar read
+  // waits inside the Q K^T chain), moved to scalar registers of the tile's
+  // stage when the codes are stored.  (The prefix pass at head size 64
+  // with 4-token blocks reads them at the tile instead: the staging
+  // registers would cost it a wave per SIMD.)
+  constexpr bool kScaleStaged = kFp8 && (kScaleBlocks <= 4 || D == 128 || !kPrefix);
+  constexpr int kSc = 2 * kScaleBlocks;
   const __amdgpu_buffer_rsrc_t ksc_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.k_scale, 0, 0x7fffffff, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vsc_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.v_scale, 0, 0x7fffffff, kBufferFlags);
-  uint32_t stg_sc[2];
-  float sc0[2], sc1[2], sc2[2];
-  auto stage_sc = [&](auto st) -> float (&)[2] {
+  uint32_t stg_sc[kSc];
+  float sc0[kSc], sc1[kSc], sc2[kSc];
+  auto stage_sc = [&](auto st) -> float (&)[kSc] {
     if constexpr (decltype(st)::value == 0) return sc0;
     else if constexpr (decltype(st)::value == 1) return sc1;
     else return sc2;
@@ -505,9 +508,20 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
       return;
     }
     if constexpr (kFp8) {
-      // Per-lane addresses over at most kRawBlocksPerLoad blocks (scalar
-      // table reads); keys past the end re-read the last key (finite data;
-      // those keys are masked).
+      // The tile's scales (one pair per block), then per-lane addresses
+      // over at most kRawBlocksPerLoad blocks (scalar table reads); keys
+      // past the end re-read the last key (finite data; those keys are
+      // masked).
+#pragma unroll
+      for (int j = 0; j < kScaleBlocks; ++j) {
+        if constexpr (kScaleStaged) {
+          const uint32_t blk =
+              table[__builtin_amdgcn_readfirstlane(min(int(unsigned(kb) / BS) + j, last_idx))];
+          const int32_t sc_off = int32_t((int64_t(blk) * H + head) * 4);
+          stg_sc[2 * j] = __builtin_amdgcn_raw_buffer_load_b32(ksc_rsrc, 0, sc_off, 0);
+          stg_sc[2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b32(vsc_rsrc, 0, sc_off, 0);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < kRawLoadsPerWave; ++j) {
         const int row0 = raw_li[j] * kRawRowsPerLoad;
@@ -595,9 +609,10 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
         *(u32x4_t*)(dst + ((2 * raw_piece + 1) ^ sw) * 16) = u32x4_t{h[4], h[5], h[6], h[7]};
       }
       if constexpr (kScaleStaged) {
-        float (&d)[2] = stage_sc(st);
-        d[0] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(stg_sc[0]));
-        d[1] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(stg_sc[1]));
+        float (&d)[kSc] = stage_sc(st);
+#pragma unroll
+        for (int j = 0; j < kSc; ++j)
+          d[j] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(stg_sc[j]));
       }
     } else {
 #pragma unroll
@@ -698,8 +713,11 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
       // issued before the MFMAs that they wait behind).
       float sk[kScaleBlocks], sv[kScaleBlocks];
       if constexpr (kScaleStaged) {
-        sk[0] = stage_sc(st)[0];
-        sv[0] = stage_sc(st)[1];
+#pragma unroll
+        for (int j = 0; j < kScaleBlocks; ++j) {
+          sk[j] = stage_sc(st)[2 * j];
+          sv[j] = stage_sc(st)[2 * j + 1];
+        }
       } else if constexpr (kFp8) {
 #pragma unroll
         for (int j = 0; j < kScaleBlocks; ++j) {
