@@ -229,7 +229,7 @@ __device__ __forceinline__ void wg_barrier() {
 // that of the scaled weights to fp16.
 template <int KV, int QT, int D, int BS, bool kPrefix = false>
 __global__ __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(((KV == PA_FP8_E4M3 && BS < 32) || (KV == PA_F16 && D == 128 && BS == 4)) ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(((KV == PA_FP8_E4M3 && BS < 8) || (KV == PA_F16 && D == 128 && BS == 4)) ? 2 : 3)))
 void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq) {
   constexpr bool kFp8 = KV == PA_FP8_E4M3;
   constexpr int kRowBytes = D * 2;
@@ -503,6 +503,34 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
       for (int j = 0; j < kRawLoadsPerWave; ++j) {
         const int keyc = min(kb + raw_row[j], L - 1);
         const uint32_t off = uint32_t(unsigned(keyc) % BS) * D + raw_piece * 16;
+        dst[j] = *(const u32x4_t*)((const char*)(raw_v[j] ? a.v_cache : a.k_cache) + base + off);
+      }
+      return;
+    }
+    if constexpr (kFp8 && kRawBlocksPerLoad == 1) {
+      // Each raw load lies in one block: the load's own block when its
+      // first row is a key (that block then holds L - 1 if the rows reach
+      // past it), else the last block.  A uniform base per load, and keys
+      // past the end re-read the last key (finite data; those keys are
+      // masked) through a clamped 32-bit lane offset.
+#pragma unroll
+      for (int j = 0; j < kScaleBlocks; ++j) {
+        if constexpr (kScaleStaged) {
+          const uint32_t blk =
+              table[__builtin_amdgcn_readfirstlane(min(int(unsigned(kb) / BS) + j, last_idx))];
+          const int32_t sc_off = int32_t((int64_t(blk) * H + head) * 4);
+          stg_sc[2 * j] = __builtin_amdgcn_raw_buffer_load_b32(ksc_rsrc, 0, sc_off, 0);
+          stg_sc[2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b32(vsc_rsrc, 0, sc_off, 0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kRawLoadsPerWave; ++j) {
+        const int row0 = raw_li[j] * kRawRowsPerLoad;
+        const uint32_t blk =
+            table[__builtin_amdgcn_readfirstlane(min(int(unsigned(kb + row0) / BS), last_idx))];
+        const int keyc = min(kb + raw_row[j], L - 1);
+        const uint32_t off = uint32_t(unsigned(keyc) % BS) * D + raw_piece * 16;
+        const int64_t base = int64_t(blk) * blk_stride + head_off;
         dst[j] = *(const u32x4_t*)((const char*)(raw_v[j] ? a.v_cache : a.k_cache) + base + off);
       }
       return;
