@@ -229,7 +229,7 @@ __device__ __forceinline__ void wg_barrier() {
 // that of the scaled weights to fp16.
 template <int KV, int QT, int D, int BS, bool kPrefix = false>
 __global__ __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(((KV == PA_FP8_E4M3 && BS < 8) || (KV == PA_F16 && D == 128 && BS == 4)) ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu((KV == PA_FP8_E4M3 && BS < 8) ? 2 : 3)))
 void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq) {
   constexpr bool kFp8 = KV == PA_FP8_E4M3;
   constexpr int kRowBytes = D * 2;
