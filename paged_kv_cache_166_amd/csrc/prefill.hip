@@ -486,6 +486,18 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
     else if constexpr (decltype(st)::value == 1) return sc1;
     else return sc2;
   };
+  // The K and V scales of the kScaleBlocks blocks of the tile at key kb
+  // into the staging registers.
+  auto load_scales = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < kScaleBlocks; ++j) {
+      const uint32_t blk =
+          table[__builtin_amdgcn_readfirstlane(min(int(unsigned(kb) / BS) + j, last_idx))];
+      const int32_t sc_off = int32_t((int64_t(blk) * H + head) * 4);
+      stg_sc[2 * j] = __builtin_amdgcn_raw_buffer_load_b32(ksc_rsrc, 0, sc_off, 0);
+      stg_sc[2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b32(vsc_rsrc, 0, sc_off, 0);
+    }
+  };
   auto load_tile = [&](u32x4_t (&dst)[kStage], int t, uint32_t blk_hint) {
     const int kb = (t0 + t) * kBN;
     if constexpr (kFp8 && BS >= kBN) {
@@ -494,11 +506,11 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
       // entry of kb, which holds L - 1 whenever the tile reaches past it:
       // a uniform base, and keys past the end re-read the last key (finite
       // data; those keys are masked).
-      const uint32_t blk = table[__builtin_amdgcn_readfirstlane(int(unsigned(kb) / BS))];
+      // (the min never clamps; it makes this the entry load_scales reads)
+      const uint32_t blk =
+          table[__builtin_amdgcn_readfirstlane(min(int(unsigned(kb) / BS), last_idx))];
       const int64_t base = int64_t(blk) * blk_stride + head_off;
-      const int32_t sc_off = int32_t((int64_t(blk) * H + head) * 4);
-      stg_sc[0] = __builtin_amdgcn_raw_buffer_load_b32(ksc_rsrc, 0, sc_off, 0);
-      stg_sc[1] = __builtin_amdgcn_raw_buffer_load_b32(vsc_rsrc, 0, sc_off, 0);
+      load_scales(kb);
 #pragma unroll
       for (int j = 0; j < kRawLoadsPerWave; ++j) {
         const int keyc = min(kb + raw_row[j], L - 1);
@@ -513,16 +525,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
       // past it), else the last block.  A uniform base per load, and keys
       // past the end re-read the last key (finite data; those keys are
       // masked) through a clamped 32-bit lane offset.
-#pragma unroll
-      for (int j = 0; j < kScaleBlocks; ++j) {
-        if constexpr (kScaleStaged) {
-          const uint32_t blk =
-              table[__builtin_amdgcn_readfirstlane(min(int(unsigned(kb) / BS) + j, last_idx))];
-          const int32_t sc_off = int32_t((int64_t(blk) * H + head) * 4);
-          stg_sc[2 * j] = __builtin_amdgcn_raw_buffer_load_b32(ksc_rsrc, 0, sc_off, 0);
-          stg_sc[2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b32(vsc_rsrc, 0, sc_off, 0);
-        }
-      }
+      if constexpr (kScaleStaged) load_scales(kb);
 #pragma unroll
       for (int j = 0; j < kRawLoadsPerWave; ++j) {
         const int row0 = raw_li[j] * kRawRowsPerLoad;
@@ -540,16 +543,7 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
       // over at most kRawBlocksPerLoad blocks (scalar table reads); keys
       // past the end re-read the last key (finite data; those keys are
       // masked).
-#pragma unroll
-      for (int j = 0; j < kScaleBlocks; ++j) {
-        if constexpr (kScaleStaged) {
-          const uint32_t blk =
-              table[__builtin_amdgcn_readfirstlane(min(int(unsigned(kb) / BS) + j, last_idx))];
-          const int32_t sc_off = int32_t((int64_t(blk) * H + head) * 4);
-          stg_sc[2 * j] = __builtin_amdgcn_raw_buffer_load_b32(ksc_rsrc, 0, sc_off, 0);
-          stg_sc[2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b32(vsc_rsrc, 0, sc_off, 0);
-        }
-      }
+      if constexpr (kScaleStaged) load_scales(kb);
 #pragma unroll
       for (int j = 0; j < kRawLoadsPerWave; ++j) {
         const int row0 = raw_li[j] * kRawRowsPerLoad;
@@ -737,8 +731,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
     if (active) {
       const uint4 kf0 = kfrag(0);
       const char* vl = stage_v(st);
-      // fp8 pools: the K and V scales of the tile's blocks (scalar reads,
-      // issued before the MFMAs that they wait behind).
+      // fp8 pools: the K and V scales of the tile's blocks (staged with its
+      // codes, else scalar reads issued before the MFMAs that wait for them).
       float sk[kScaleBlocks], sv[kScaleBlocks];
       if constexpr (kScaleStaged) {
 #pragma unroll
