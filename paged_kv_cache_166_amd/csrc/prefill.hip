@@ -942,7 +942,8 @@ void prefill_kernel(PrefillArgs a, int num_qtiles, int num_pairs, int lpt_by_seq
 
 // Workgroups of prefill_kernel<KV, QT, D, BS> resident on the GPU at once
 // (per CU by its registers and LDS, times the CUs), looked up once per
-// instantiation on the first launch's device; 0 if the runtime cannot say.
+// instantiation on the first launch's device; 0 if the runtime cannot say
+// (its error is then cleared, so that the launch's own status is reported).
 template <int KV, int QT, int D, int BS>
 int64_t resident_workgroups() {
   static const int64_t n = [] {
@@ -950,8 +951,10 @@ int64_t resident_workgroups() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel<KV, QT, D, BS>,
                                                      kWaves * 64, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
       return int64_t(0);
+    }
     return int64_t(per_cu) * cus;
   }();
   return n;
