@@ -35,19 +35,37 @@ __device__ __forceinline__ void load8_f32(const void* p, int dt, float* x) {
   }
 }
 
+// kNarrow: the call's (token, head, chunk) count fits 32 bits, so the index
+// splits in 32-bit arithmetic (64-bit division is a long instruction
+// sequence).  head_dim / 8 and block_size are powers of two (checked on the
+// host): shifts and masks.
+template <bool kNarrow>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
-  const int chunks = a.head_dim / 8;
-  const int64_t n = int64_t(a.num_tokens) * a.num_heads * chunks;
-  const int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
-  if (idx >= n) return;
-  const int c = int(idx % chunks);
-  const int64_t th = idx / chunks;
-  const int h = int(th % a.num_heads);
-  const int64_t t = th / a.num_heads;
+  const int cl = __builtin_ctz(unsigned(a.head_dim) / 8u);   // log2(chunks per row)
+  const int bl = __builtin_ctz(unsigned(a.block_size));
+  int c, h;
+  int64_t t;
+  if constexpr (kNarrow) {
+    const uint32_t n = (uint32_t(a.num_tokens) * uint32_t(a.num_heads)) << cl;
+    const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+    if (idx >= n) return;
+    c = int(idx & ((1u << cl) - 1u));
+    const uint32_t th = idx >> cl;
+    h = int(th % uint32_t(a.num_heads));
+    t = int64_t(th / uint32_t(a.num_heads));
+  } else {
+    const int64_t n = (int64_t(a.num_tokens) * a.num_heads) << cl;
+    const int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+    if (idx >= n) return;
+    c = int(idx & ((int64_t(1) << cl) - 1));
+    const int64_t th = idx >> cl;
+    h = int(th % a.num_heads);
+    t = th / a.num_heads;
+  }
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
-  const int64_t blk = slot / a.block_size;
-  const int64_t off = slot % a.block_size;
+  const int64_t blk = slot >> bl;
+  const int64_t off = slot & (a.block_size - 1);
   const int64_t src_e = (t * a.num_heads + h) * a.head_dim + c * 8;
   const int64_t dst_e = ((blk * a.num_heads + h) * a.block_size + off) * a.head_dim + c * 8;
   const int in_b = dtype_bytes(a.in_dtype);
@@ -221,7 +239,12 @@ hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream)
   }
   const int64_t groups = (n + 255) / 256;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;   // the grid's x limit
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(unsigned(groups)), dim3(256), 0, stream, a);
+  if (n <= 0xffffffffll)
+    hipLaunchKernelGGL(reshape_and_cache_kernel<true>, dim3(unsigned(groups)), dim3(256), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel<false>, dim3(unsigned(groups)), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
